@@ -1,0 +1,10 @@
+"""Reference (oracle) implementation of the MoDA forward pass.
+
+Test infrastructure only: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product path.
+"""
+from .moda_oracle import (  # noqa: F401
+    moda_forward,
+    moda_forward_scalar,
+    depth_utilisation,
+)
