@@ -1,0 +1,15 @@
+"""MoDA (mixture-of-depths attention) forward for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+libmoda.so (include/moda.h); this package only marshals tensors into it.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MODA_BF16,
+    MODA_F32,
+    ModaError,
+    load,
+    status_string,
+)
+from .ops import depth_packed_elems, moda_fwd, moda_pack_depth  # noqa: F401

@@ -1,0 +1,107 @@
+// C ABI of libmoda.so (declared in include/moda.h): argument validation,
+// kernel selection and launch on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "moda.h"
+#include "moda_fwd.hpp"
+#include "moda_pack.hpp"
+
+namespace {
+
+constexpr int kWaves = 4;          // waves per workgroup of the forward kernel
+constexpr int kRowsPerTile = 32 * kWaves;
+
+bool valid_dtype(int dtype) { return dtype == MODA_F32 || dtype == MODA_BF16; }
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+long long padded_depth_keys(int T, int L_d) {
+  const long long n = (long long)T * L_d;
+  return (n + 31) / 32 * 32;
+}
+
+template <typename E, int D>
+hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((moda::moda_fwd_kernel<E, D, kWaves>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_pack(const moda::PackParams& p, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((moda::moda_pack_depth_kernel<E, D>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moda_status_string(int status) {
+  switch (status) {
+    case MODA_OK: return "MODA_OK";
+    case MODA_ERR_NULL: return "MODA_ERR_NULL: a required pointer is NULL";
+    case MODA_ERR_SHAPE: return "MODA_ERR_SHAPE: a size is out of range or inconsistent";
+    case MODA_ERR_DTYPE: return "MODA_ERR_DTYPE: unknown dtype";
+    case MODA_ERR_UNSUPPORTED: return "MODA_ERR_UNSUPPORTED: head size must be 64 or 128";
+    case MODA_ERR_HIP: return "MODA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown moda_status";
+  }
+}
+
+long long moda_depth_packed_elems(int B, int T, int Hkv, int d, int L_d) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_d < 0) return -1;
+  return (long long)B * Hkv * padded_depth_keys(T, L_d) * d;
+}
+
+int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, void* v_packed,
+                    int B, int T, int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (L_d == 0) return MODA_OK;
+  if (!k_depth || !v_depth || !k_packed || !v_packed) return MODA_ERR_NULL;
+  moda::PackParams p{k_depth, v_depth, k_packed, v_packed, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
+  const long long grid = (long long)B * Hkv * (p.NKp / 32);
+  if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == MODA_BF16)
+    e = d == 128 ? launch_pack<moda::bf16, 128>(p, (unsigned)grid, s) : launch_pack<moda::bf16, 64>(p, (unsigned)grid, s);
+  else
+    e = d == 128 ? launch_pack<float, 128>(p, (unsigned)grid, s) : launch_pack<float, 64>(p, (unsigned)grid, s);
+  return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+             const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
+             int L_d, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (!q || !k_seq || !v_seq || !out) return MODA_ERR_NULL;
+  if (L_d > 0 && (!k_depth || !v_depth)) return MODA_ERR_NULL;
+  const int G = Hq / Hkv;
+  const long long rows = (long long)T * G;
+  const long long ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
+  const long long grid = ntiles * B * Hkv;
+  if (grid > 0x7fffffffLL || rows > 0x7fffffffLL) return MODA_ERR_SHAPE;
+
+  moda::FwdParams p;
+  p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
+  p.out = out; p.lse = lse;
+  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.L_d = L_d;
+  p.ntiles = (int)ntiles;
+  p.NKp = padded_depth_keys(T, L_d);
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == MODA_BF16)
+    e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)grid, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, s);
+  else
+    e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, s) : launch_fwd<float, 64>(p, (unsigned)grid, s);
+  return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+}  // extern "C"

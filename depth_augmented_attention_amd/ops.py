@@ -1,0 +1,114 @@
+"""Tensor-level binding of the C ABI: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libmoda.so; torch
+provides device memory and the current stream.  There is no fallback path:
+if the library is missing or the tensors are not on a GPU these calls raise.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import MODA_BF16, MODA_F32, check, load
+
+_DT = {torch.float32: MODA_F32, torch.bfloat16: MODA_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def depth_packed_elems(B: int, T: int, Hkv: int, d: int, L_d: int) -> int:
+    n = load().moda_depth_packed_elems(B, T, Hkv, d, L_d)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def moda_pack_depth(k_depth: torch.Tensor, v_depth: torch.Tensor,
+                    k_packed: torch.Tensor | None = None, v_packed: torch.Tensor | None = None,
+                    stream=None):
+    """Repack depth KV [B,T,L_d,Hkv,d] into the fused kernel's layout.
+
+    Returns (k_packed, v_packed), flat tensors of depth_packed_elems(...)
+    elements each (allocated here when not given).
+    """
+    if k_depth.dim() != 5 or v_depth.shape != k_depth.shape or v_depth.dtype != k_depth.dtype:
+        raise ValueError("k_depth / v_depth must both be [B,T,L_d,Hkv,d] of one dtype")
+    B, T, L_d, Hkv, d = k_depth.shape
+    n = depth_packed_elems(B, T, Hkv, d, L_d)
+    if k_packed is None:
+        k_packed = torch.empty(n, dtype=k_depth.dtype, device=k_depth.device)
+    if v_packed is None:
+        v_packed = torch.empty(n, dtype=k_depth.dtype, device=k_depth.device)
+    if L_d == 0:
+        return k_packed, v_packed
+    for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth"), (k_packed, "k_packed"), (v_packed, "v_packed")):
+        _dev(t, name)
+    if k_packed.numel() != n or v_packed.numel() != n or k_packed.dtype != k_depth.dtype \
+            or v_packed.dtype != k_depth.dtype:
+        raise ValueError(f"packed buffers must hold {n} elements of {k_depth.dtype}")
+    st = load().moda_pack_depth(k_depth.data_ptr(), v_depth.data_ptr(), k_packed.data_ptr(),
+                                v_packed.data_ptr(), B, T, Hkv, d, L_d, _dtype_code(k_depth),
+                                _stream(stream))
+    check(st, "moda_pack_depth")
+    return k_packed, v_packed
+
+
+def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+             k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+             with_lse: bool = True, stream=None):
+    """MoDA forward.  q [B,T,Hq,d]; k_seq, v_seq [B,T,Hkv,d]; k_depth, v_depth
+    are the packed buffers from moda_pack_depth (None when L_d == 0).
+
+    Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
+    """
+    if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
+        raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
+    B, T, Hq, d = q.shape
+    Hkv = k_seq.shape[2]
+    if k_seq.shape[:2] != (B, T) or k_seq.shape[3] != d:
+        raise ValueError("k_seq shape does not match q")
+    if k_seq.dtype != q.dtype or v_seq.dtype != q.dtype:
+        raise ValueError("q, k_seq, v_seq must share one dtype")
+    for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq")):
+        _dev(t, name)
+    kd_ptr = vd_ptr = None
+    if L_d > 0:
+        if k_depth is None or v_depth is None:
+            raise ValueError("packed depth buffers are required when L_d > 0")
+        n = depth_packed_elems(B, T, Hkv, d, L_d)
+        for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+            _dev(t, name)
+            if t.numel() != n or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
+        kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    if with_lse and lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse")
+        if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
+            raise ValueError("lse must be float32 [B,Hq,T]")
+    st = load().moda_fwd(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+                         out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                         B, T, Hq, Hkv, d, L_d, _dtype_code(q), _stream(stream))
+    check(st, "moda_fwd")
+    return out, lse

@@ -1,0 +1,126 @@
+/*
+ * moda.h -- C ABI of libmoda.so: the forward pass of Mixture-of-Depths
+ * Attention (MoDA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (mhpn.cn article "动态混合深度注意力机制MoDA技术解析", section
+ * 1.2, MoDA attention formula; section 2.2, dual masks; gist.science (de)
+ * "Mixture-of-Depths Attention", Technische Zusammenfassung section 2,
+ * Read-Step and Unified Softmax):
+ *
+ *   for every batch b, position t, query head h (kv head kvh = h / G,
+ *   G = Hq / Hkv):
+ *     keys   = [ k_seq[b, 0..t, kvh, :] ; k_depth[b, t, 0..L_d-1, kvh, :] ]
+ *     values = [ v_seq[b, 0..t, kvh, :] ; v_depth[b, t, 0..L_d-1, kvh, :] ]
+ *     z      = keys . q[b, t, h, :] / sqrt(d)
+ *     out[b, t, h, :] = softmax(z) . values          (one softmax over both)
+ *     lse[b, h, t]    = log(sum(exp(z)))             (natural log)
+ *
+ * i.e. causal sequence attention (s <= t) of the current layer joined with the
+ * L_d depth slots that earlier layers wrote for the SAME position t.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers (HIP device memory of the current
+ *     device), owned by the caller.  The library allocates nothing and keeps
+ *     no state between calls; calls on different streams may run concurrently.
+ *   - Tensors are dense, row-major, in the layouts stated per argument
+ *     (no strides).  Element type is `dtype` (MODA_F32 or MODA_BF16) except
+ *     lse, which is always float32.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Every call only enqueues work and returns; results are ready
+ *     after the stream is synchronised.
+ *   - Arguments are validated before any HIP call is made.  A failed
+ *     validation returns a nonzero moda_status and enqueues nothing.  A
+ *     failed kernel launch returns MODA_ERR_HIP.  Faults inside a kernel
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Supported: dtype MODA_F32 or MODA_BF16, head size d = 64 or 128,
+ *     any B, T >= 1, Hkv >= 1 with Hq a multiple of Hkv (G = 1 .. Hq),
+ *     L_d >= 0.  Inputs are expected to be finite.
+ */
+#ifndef MODA_H
+#define MODA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MODA_F32 = 0,
+  MODA_BF16 = 1
+} moda_dtype;
+
+typedef enum {
+  MODA_OK = 0,
+  MODA_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  MODA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent      */
+  MODA_ERR_DTYPE = 3,       /* unknown dtype                                */
+  MODA_ERR_UNSUPPORTED = 4, /* valid but not built (head size not 64/128)   */
+  MODA_ERR_HIP = 5          /* the HIP runtime reported an error on launch  */
+} moda_status;
+
+/*
+ * Number of ELEMENTS of each packed depth tensor (the packed keys and the
+ * packed values have the same size): B * Hkv * NKp * d where NKp is T * L_d
+ * rounded up to a multiple of 32.  Returns -1 for invalid sizes, 0 when
+ * L_d == 0.
+ */
+long long moda_depth_packed_elems(int B, int T, int Hkv, int d, int L_d);
+
+/*
+ * moda_pack_depth -- repack the depth KV into the kernel's layout.
+ *
+ * The depth slots of one token position are the K/V that the L_d earlier
+ * layers wrote for that position (gist.science (de), section 2, Read-Step and
+ * Write-Step).  The pages flatten depth KV along one T x L axis so that it can
+ * be read block-wise, and store the slots of one position contiguously
+ * (gist.science (de), section 2, Flash-Compatible Layout; mhpn.cn article,
+ * section 2.1, chunked contiguous storage).  This call produces that layout
+ * for each (b, kv head):
+ *
+ *   k_depth, v_depth : in,  logical [B, T, L_d, Hkv, d], dtype
+ *   k_packed         : out, [B, Hkv, NKp, d]            key n = t * L_d + j
+ *   v_packed         : out, [B, Hkv, NKp / 32, d, 32]   the same keys in
+ *                      chunks of 32, each chunk stored d-major (value
+ *                      transposed), as the fused kernel's matrix-core operand
+ *                      wants it.
+ *   Keys n >= T * L_d (padding up to NKp) are written as zeros.
+ *   Each packed buffer holds moda_depth_packed_elems(...) elements.
+ *
+ * With L_d == 0 nothing is enqueued and all four pointers may be NULL.
+ * The packed buffers must not overlap the inputs.
+ */
+int moda_pack_depth(const void* k_depth, const void* v_depth,
+                    void* k_packed, void* v_packed,
+                    int B, int T, int Hkv, int d, int L_d, int dtype,
+                    void* stream);
+
+/*
+ * moda_fwd -- fused MoDA forward.
+ *
+ *   q        : in,  [B, T, Hq, d]  dtype
+ *   k_seq    : in,  [B, T, Hkv, d] dtype   (current layer's sequence keys)
+ *   v_seq    : in,  [B, T, Hkv, d] dtype
+ *   k_depth  : in,  packed keys   from moda_pack_depth (NULL iff L_d == 0)
+ *   v_depth  : in,  packed values from moda_pack_depth (NULL iff L_d == 0)
+ *   out      : out, [B, T, Hq, d]  dtype   (rounded to nearest even for bf16)
+ *   lse      : out, [B, Hq, T] float32, natural-log sum of exp of the scaled
+ *              scores; may be NULL to skip it
+ *   B, T, Hq, Hkv, d, L_d, dtype : sizes as above
+ *
+ * Scores are computed with float32 accumulation; softmax statistics and the
+ * output accumulator are float32.  With L_d == 0 the call is causal GQA
+ * attention, run by the same kernel.  out must not overlap any input.
+ */
+int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
+             const void* k_depth, const void* v_depth,
+             void* out, float* lse,
+             int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+             void* stream);
+
+/* Static, human-readable name of a moda_status value. */
+const char* moda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MODA_H */

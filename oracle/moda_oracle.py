@@ -93,20 +93,26 @@ def moda_forward(q, k_seq, v_seq, k_depth, v_depth,
     0..L_d-1).  Only meant for tiny shapes.
 
     One (b, t, kv-head) group at a time: the G query rows of that group are
-    scored against the explicitly concatenated key set
-        Kc = [k_seq[b, 0..t, kvh] ; k_depth[b, t, 0..L_d-1, kvh]]
-    (mhpn.cn article, section 1.2 formula; section 2.2 masks), the scores are
-    scaled by 1/sqrt(d), and a single softmax is taken over all of them
-    (gist.science (de), section 2, Unified Softmax).
+    scored against the concatenated key set
+        [k_seq[b, 0..t, kvh] ; k_depth[b, t, 0..L_d-1, kvh]]
+    (mhpn.cn article, section 1.2 formula; section 2.2 masks) as the
+    concatenation of the two score blocks, the scores are scaled by 1/sqrt(d),
+    and a single softmax is taken over all of them (gist.science (de),
+    section 2, Unified Softmax).
     """
-    q = _f64(q)
-    k_seq = _f64(k_seq)
-    v_seq = _f64(v_seq)
-    k_depth = _f64(k_depth)
-    v_depth = _f64(v_depth)
+    q = np.asarray(q)
+    k_seq = np.asarray(k_seq)
+    v_seq = np.asarray(v_seq)
+    k_depth = np.asarray(k_depth)
+    v_depth = np.asarray(v_depth)
     B, T, Hq, Hkv, d, L_d = _check_shapes(q, k_seq, v_seq, k_depth, v_depth)
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(d)
+    # Sequence keys / values of each (b, kv head) as contiguous float64
+    # [B, Hkv, T, d] (an exact conversion; only the layout changes), so that
+    # the prefix 0..t of one head is a plain contiguous slice.
+    Kseq = _f64(np.ascontiguousarray(np.transpose(k_seq, (0, 2, 1, 3))))
+    Vseq = _f64(np.ascontiguousarray(np.transpose(v_seq, (0, 2, 1, 3))))
 
     if rows is None:
         groups = {}
@@ -128,17 +134,26 @@ def moda_forward(q, k_seq, v_seq, k_depth, v_depth,
     res_lse = {}
     res_p = {}
     for (b, t, kvh), heads in groups.items():
-        # Concatenated key / value sets of this position (sequence part:
-        # causal, s <= t; depth part: this position's slots only).
-        Kc = np.concatenate([k_seq[b, : t + 1, kvh, :], k_depth[b, t, :, kvh, :]], axis=0)
-        Vc = np.concatenate([v_seq[b, : t + 1, kvh, :], v_depth[b, t, :, kvh, :]], axis=0)
-        Qg = q[b, t, heads, :]                      # [g, d]
-        z = (Qg @ Kc.T) * scale                     # [g, n], n = t + 1 + L_d
+        # The key set of position t: sequence keys s = 0..t of this layer
+        # (causal mask), then the L_d depth slots of position t itself
+        # (depth mask).
+        Ks = Kseq[b, kvh, : t + 1]                  # [t+1, d]
+        Vs = Vseq[b, kvh, : t + 1]
+        Kd = _f64(k_depth[b, t, :, kvh, :])         # [L_d, d]
+        Vd = _f64(v_depth[b, t, :, kvh, :])
+        Qg = _f64(q[b, t, heads, :])                # [g, d]
+        # Scores: the concatenation [Q K_seq^T || Q K_depth^T], scaled by
+        # 1/sqrt(d) as a whole (mhpn.cn article, section 1.2 formula).
+        z = np.concatenate([Qg @ Ks.T, Qg @ Kd.T], axis=1) * scale   # [g, t+1+L_d]
+        # One softmax over the whole concatenation (Unified Softmax).
         m = z.max(axis=1, keepdims=True)
         e = np.exp(z - m)
         Z = e.sum(axis=1, keepdims=True)
         p = e / Z
-        o = p @ Vc                                  # [g, d]
+        # p times the concatenated values [V_seq ; V_depth]: the product with
+        # a concatenation is the sum of the two block products.
+        ns = t + 1
+        o = p[:, :ns] @ Vs + p[:, ns:] @ Vd         # [g, d]
         lse = m[:, 0] + np.log(Z[:, 0])
         for i, h in enumerate(heads):
             res_out[(b, t, h)] = o[i]

@@ -1,0 +1,98 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects invalid arguments before making any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import depth_augmented_attention_amd as moda
+from depth_augmented_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moda.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_matches_binding():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    lib = moda.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moda_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_status_strings():
+    for code in range(6):
+        assert moda.status_string(code).startswith("MODA_")
+    assert "unknown" in moda.status_string(99)
+
+
+def test_packed_elems():
+    lib = moda.load()
+    assert lib.moda_depth_packed_elems(1, 128, 1, 64, 3) == 128 * 3 * 64
+    assert lib.moda_depth_packed_elems(3, 77, 3, 128, 5) == 3 * 3 * 416 * 128   # 385 -> 416
+    assert lib.moda_depth_packed_elems(1, 65536, 2, 128, 24) == 2 * 65536 * 24 * 128
+    assert lib.moda_depth_packed_elems(1, 5, 1, 64, 0) == 0
+    assert lib.moda_depth_packed_elems(0, 5, 1, 64, 1) == -1
+    assert lib.moda_depth_packed_elems(1, 5, 1, 64, -1) == -1
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,code", [
+    # q, k, v, kd, vd, out, lse, B, T, Hq, Hkv, d, L_d, dtype
+    ((None, FAKE, FAKE, None, None, FAKE, None, 1, 4, 2, 1, 128, 0, 1), _lib.MODA_ERR_NULL),
+    ((FAKE, FAKE, FAKE, None, None, None, None, 1, 4, 2, 1, 128, 0, 1), _lib.MODA_ERR_NULL),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 4, 2, 1, 128, 3, 1), _lib.MODA_ERR_NULL),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 4, 3, 2, 128, 0, 1), _lib.MODA_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 0, 2, 1, 128, 0, 1), _lib.MODA_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 0, 4, 2, 1, 128, 0, 1), _lib.MODA_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 4, 2, 1, 128, -1, 1), _lib.MODA_ERR_SHAPE),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 4, 2, 1, 128, 0, 7), _lib.MODA_ERR_DTYPE),
+    ((FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 4, 2, 1, 96, 0, 1), _lib.MODA_ERR_UNSUPPORTED),
+])
+def test_fwd_validation(args, code):
+    lib = moda.load()
+    assert lib.moda_fwd(*args, None) == code
+
+
+def test_pack_validation():
+    lib = moda.load()
+    # L_d == 0: nothing to do, NULL pointers allowed, no HIP call
+    assert lib.moda_pack_depth(None, None, None, None, 1, 4, 1, 128, 0, 1, None) == _lib.MODA_OK
+    assert lib.moda_pack_depth(None, FAKE, FAKE, FAKE, 1, 4, 1, 128, 2, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_pack_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 100, 2, 1, None) == _lib.MODA_ERR_UNSUPPORTED
+    assert lib.moda_pack_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 2, 5, None) == _lib.MODA_ERR_DTYPE
+    assert lib.moda_pack_depth(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 128, 2, 1, None) == _lib.MODA_ERR_SHAPE
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moda.moda_fwd(q, k, k, None, None, 0)
+
+
+def test_product_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "depth_augmented_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in src.lower(), f"{f} mentions the oracle"
