@@ -1,0 +1,254 @@
+"""Benchmark of the MoDA forward hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the depth repack (moda_pack_depth) followed by the fused forward (moda_fwd).
+Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0, one GPU):
+  value        useful TFLOP/s of the step (pack + fwd),
+               useful FLOPs = 4 * B * Hq * d * (T (T+1) / 2 + T * L_d)
+  roofline     the fused forward kernel against the bf16 dense matrix-core
+               peak, from HIP events around each launch in the timed region
+  cpu_baseline the oracle timed on the host on a bounded sample of rows
+plus the forward-only rate, the repack time and bandwidth, and the forward
+time of the same kernel at L_d = 0 (overhead of the depth slots).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoDA fwd TFLOP/s (bf16, T=64K) + % MFMA peak; overhead vs L_d=0"
+DEFAULT_WORKLOAD = "bf16_B1_T65536_Hq16_Hkv2_d128_L24"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix-core peaks
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def useful_flops(B, T, Hq, d, L_d, rows=None):
+    """QK^T and PV multiply-adds of unmasked scores, 2 flops each."""
+    if rows is None:
+        return 4.0 * B * Hq * d * (T * (T + 1) / 2 + T * L_d)
+    return float(sum(4.0 * d * (int(t) + 1 + L_d) for (_, t, _) in rows))
+
+
+def compulsory_bytes(w):
+    eb = 2 if w["dtype"] == "bf16" else 4
+    B, T, Hq, Hkv, d, L = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
+    return eb * (2 * B * T * Hq * d + 2 * B * T * Hkv * d + 2 * B * T * L * Hkv * d) + 4 * B * Hq * T
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "depth_augmented_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per fused-forward launch from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"moda_fwd_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """Oracle rate on a bounded, seeded sample of query rows of the workload."""
+    import numpy as np
+    import torch
+
+    from moda_inputs import sample_rows
+    from oracle import moda_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, ks, vs, kd, vd = [x.to(torch.float32).numpy() for x in inputs]
+    rows = sample_rows(w["B"], w["T"], w["Hq"], n=65536, seed=w["seed"] + 11)
+    rng = np.random.default_rng(w["seed"] + 12)
+    rows = rows[rng.permutation(len(rows))]
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    chunk = 64
+    while done < len(rows) and time.perf_counter() - t0 < budget_s:
+        sel = rows[done:done + chunk]
+        moda_forward(q, ks, vs, kd, vd, rows=sel)
+        flops += useful_flops(w["B"], w["T"], w["Hq"], w["d"], w["L_d"], rows=sel)
+        done += len(sel)
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} seeded random (b,t,h) query rows of {w['name']} "
+                  f"(float64 numpy oracle, {dt:.1f} s; rate = useful FLOPs of those rows / time)",
+        "rows_per_s": done / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-l0", action="store_true", help="skip the L_d = 0 comparison")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the fused kernel's sharding across GPUs is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import depth_augmented_attention_amd as moda
+    from moda_inputs import make_workload_inputs, workload
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB")
+        return
+
+    w = workload(args.workload)
+    B, T, Hq, Hkv, d, L_d = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
+    log(f"workload {w['name']}: generating seeded inputs")
+    inputs = make_workload_inputs(w)
+    q, ks, vs, kd, vd = [x.to(dev) for x in inputs]
+    kp = torch.empty(moda.depth_packed_elems(B, T, Hkv, d, L_d), dtype=q.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        moda.moda_pack_depth(kd, vd, kp, vp)
+        if ev is not None:
+            ev[1].record()
+        moda.moda_fwd(q, ks, vs, kp, vp, L_d, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pack_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    avg_fwd = sum(fwd_ms) / len(fwd_ms)
+    avg_pack = sum(pack_ms) / len(pack_ms)
+    F = useful_flops(B, T, Hq, d, L_d)
+    log(f"step {ms_per_step:.3f} ms  fwd {avg_fwd:.3f} ms  pack {avg_pack:.3f} ms")
+
+    res = {
+        "metric": METRIC,
+        "value": F / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded i.i.d. N(0,1), rounded to bf16)",
+        "config": {"workload": w["name"], "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "L_d": L_d,
+                   "step": "moda_pack_depth + moda_fwd"},
+    }
+    fwd_tflops = F / (avg_fwd * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w["dtype"]]
+    traffic = measured_traffic(w["name"])
+    res["roofline"] = {
+        "bound": "mfma",
+        "kernel": "moda_fwd_bf16_kernel" if w["dtype"] == "bf16" else "moda_fwd_kernel",
+        "achieved": fwd_tflops,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": fwd_tflops / peak,
+        "traffic": traffic,
+        "avg_launch_ms": avg_fwd,
+    }
+    res["fwd_ms"] = avg_fwd
+    res["fwd_tflops"] = fwd_tflops
+    res["pct_mfma_peak"] = 100.0 * fwd_tflops / peak
+    res["pack_ms"] = avg_pack
+    res["pack_gbps"] = 2 * 2 * kd.numel() * kd.element_size() / (avg_pack * 1e-3) / 1e9
+    res["fwd_compulsory_gbps"] = compulsory_bytes(w) / (avg_fwd * 1e-3) / 1e9
+
+    if not args.no_l0 and L_d > 0:
+        log("timing the same kernel at L_d = 0")
+        for _ in range(2):
+            moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
+        torch.cuda.synchronize()
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        e0[0].record()
+        for i in range(args.steps):
+            moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
+            e0[i + 1].record()
+        torch.cuda.synchronize()
+        l0 = [e0[i].elapsed_time(e0[i + 1]) for i in range(args.steps)]
+        avg_l0 = sum(l0) / len(l0)
+        res["fwd_ms_L0"] = avg_l0
+        res["fwd_tflops_L0"] = useful_flops(B, T, Hq, d, 0) / (avg_l0 * 1e-3) / 1e12
+        res["overhead_vs_L0"] = avg_fwd / avg_l0 - 1.0
+        res["overhead_vs_L0_with_pack"] = (avg_fwd + avg_pack) / avg_l0 - 1.0
+        log(f"L_d=0 fwd {avg_l0:.3f} ms, overhead {100 * res['overhead_vs_L0']:.2f}%")
+
+    if not args.no_cpu_baseline:
+        log(f"oracle on host cores ({args.cpu_budget:.0f} s budget)")
+        del q, ks, vs, kd, vd
+        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    res["kernel_source_hash"] = kernel_source_hash()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
