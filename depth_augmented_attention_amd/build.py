@@ -11,7 +11,7 @@ OUT = os.path.join(HERE, "libmoda.so")
 
 # -packed-fp32-ops off: no packed float32 VALU instructions in device code.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

@@ -23,7 +23,7 @@ long long padded_depth_keys(int T, int L_d) {
 
 template <typename E, int D>
 hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, hipStream_t s) {
-  if constexpr (sizeof(E) == 2)
+  if constexpr (sizeof(E) == 2 && D == 128)
     hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D>), dim3(grid), dim3(kWaves * 64), 0, s, p);
   else
     hipLaunchKernelGGL((moda::moda_fwd_kernel<E, D, kWaves>), dim3(grid), dim3(kWaves * 64), 0, s, p);

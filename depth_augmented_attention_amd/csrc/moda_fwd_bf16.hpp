@@ -1,11 +1,14 @@
 // Fused MoDA forward, bf16 inputs, for gfx950 (CDNA4).
 //
 // Same computation and row folding as the generic kernel in moda_fwd.hpp (see
-// the description there); this variant is laid out for the gfx950 memory
-// path:
-//   * K and V blocks are double-buffered in LDS: block j+1 is fetched into
-//     registers while block j is computed, then written to the other LDS
-//     stage; one workgroup barrier per block.
+// the description there); this variant is laid out for the gfx950 memory path
+// and for overlapping matrix-core and vector work:
+//   * K and V blocks go from HBM straight into LDS with the direct
+//     global->LDS 16-byte loads (no staging registers, no LDS store
+//     instructions).  K runs one block ahead of V: while block j's softmax and
+//     P.V run, the scores of block j+1 are already being formed on the matrix
+//     cores, so a wave always has independent matrix and vector work.  Two LDS
+//     stages each for K and V; one workgroup barrier per block.
 //   * V stays key-major in LDS; the P.V product reads it with the LDS
 //     transpose load (ds_read_b64_tr_b16), which hands each lane four
 //     consecutive keys of one head dimension -- the operand order the matrix
@@ -14,12 +17,12 @@
 //     XOR swizzle of the 16-byte chunk index (K: chunk ^ (row & 15);
 //     V: chunk ^ 4 * (row & 3)), chosen so that every 16-lane K read and every
 //     32-lane transposed V read touches 64 distinct banks.
-//   * At most 256 registers per wave, so two workgroups share a compute unit
-//     and one wave's softmax overlaps the other's matrix-core work.
+//   * At most 256 registers per wave, so two workgroups share a compute unit.
 //   * The running max is only moved (and O rescaled) when a new score exceeds
 //     it by more than 2^8; until then probabilities are taken against the
 //     stale max, which changes nothing in exact arithmetic (out = O / l and
 //     lse = m + log2 l use the same m) and keeps them <= 256.
+//   * The causal mask is only evaluated in the last few blocks of a tile.
 #pragma once
 
 #include "moda_common.hpp"
@@ -28,40 +31,54 @@
 namespace moda {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ s16x4 lds_read_tr(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+// Third word of a raw buffer descriptor on gfx9-family GPUs (32-bit data
+// format, no swizzle, no index stride).
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane l's data lands
+// at ldst + 16 l (ldst is wave-uniform).  Out-of-range offsets read zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)ldst, 16, voff, 0, 0, 0);
 }
 
-// Online-softmax step with a lazily moved max (threshold 8 in log2 units).
-template <int NV, int NDT>
-__device__ __forceinline__ void online_update_lazy(float (&sv)[NV], float& m_run, float& l_run,
-                                                   f32x16 (&o)[NDT]) {
-  float mx = sv[0];
-#pragma unroll
-  for (int i = 1; i < NV; ++i) mx = fmaxf(mx, sv[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (__any(mx > m_run + 8.f)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    m_run = m_new;
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
-    sum += sv[i];
-  }
-  l_run += sum;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Eight LDS transpose reads (two per 32-row tile of O^T over d = 128) that
+// form the four V^T operand fragments of one 16-key chunk, completed before
+// returning (the wait is inside the same asm block, so no read is in flight
+// when the compiler next touches these registers).  a[dt] is this lane's
+// byte address of its first row for tile dt; the second row is 4 rows
+// (1024 bytes) further.
+template <int OFF>
+__device__ __forceinline__ void tr_read_chunk(const uint32_t (&a)[4], bf16x8 (&f)[4]) {
+  s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + 1024)
+      : "memory");
+  const s16x4 p0[2] = {r0, r1}, p1[2] = {r2, r3}, p2[2] = {r4, r5}, p3[2] = {r6, r7};
+  f[0] = *reinterpret_cast<const bf16x8*>(p0);
+  f[1] = *reinterpret_cast<const bf16x8*>(p1);
+  f[2] = *reinterpret_cast<const bf16x8*>(p2);
+  f[3] = *reinterpret_cast<const bf16x8*>(p3);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moda_fwd_bf16_kernel(FwdParams p) {
+  static_assert(D == 128, "the bf16 fast path is built for head size 128");
   constexpr int NW = 4;
   constexpr int BN = 64;                  // keys per sequence block
   constexpr int NKC = D / 16;             // 16-wide k-chunks over d
@@ -69,11 +86,9 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TILE = BN * D;            // elements of one K (or V) block
   constexpr int LOADS = TILE / 8 / (NW * 64);   // 16-byte loads per thread per block
-  static_assert(CPR == 16 || CPR == 8, "head size 64 or 128");
-  static_assert(LOADS * NW * 64 * 8 == TILE, "tile / thread mismatch");
 
-  // [stage][K | V][BN][D]
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE];
+  // K stages 0,1 then V stages 0,1; each [BN][D], swizzled
+  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,8 +115,11 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int tw_min = wave_active ? (int)(Rw / G) : T - 1;
   const int tw_max = wave_active ? (int)((Rw + 31 < TG ? Rw + 31 : TG - 1) / G) : T - 1;
   const long long Rlast = (R0 + NW * 32 < TG ? R0 + NW * 32 : TG) - 1;
+  const int t_first = (int)(R0 / G);
   const int t_last = (int)(Rlast / G);
   const int nblocks = t_last / BN + 1;
+  // blocks [0, jm) have every key <= every row's position: no mask needed
+  const int jm = (t_first + 1) / BN < nblocks ? (t_first + 1) / BN : nblocks;
 
   bf16x8 qf[NKC];
   {
@@ -113,108 +131,176 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   f32x16 o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x16{};
-  float m_run = -1e30f;
-  float l_run = 0.f;
+  float m_run = -1e30f;   // running max (log2 units of the scaled scores)
+  float l_run = 0.f;      // running sum over this lane's keys
 
   const long long kstride = (long long)p.Hkv * D;
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long long)b * T * p.Hkv + kvh) * D;
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long long)b * T * p.Hkv + kvh) * D;
 
-  // Block kb is read from HBM into registers (issued one block ahead) and
-  // written to LDS stage st after the current block's compute.  Wave w, load i
-  // covers the 1 KB LDS span (i*NW + w); lane l fills 16-byte position l of
-  // it, i.e. row r = span * (64 / CPR) + l / CPR, physical chunk l % CPR,
-  // which holds the logical chunk physical ^ swizzle(r).
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_block = [&](int kb) {
+  // Direct loads.  A K or V block is 64 rows of 256 bytes = 16 spans of 1 KB.
+  // Span sp is written by one wave-wide load: lane l fills 16-byte position
+  // l, i.e. row r = 4 sp + l / 16, physical chunk l % 16, which holds the
+  // logical chunk physical ^ swizzle(r).  Byte offsets are lane constants
+  // relative to the block's first row; the block base lives in the (scalar)
+  // buffer descriptor.
+  uint32_t offk[LOADS], offv[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int span = i * NW + wave;
-      const int r = span * (64 / CPR) + lane / CPR;
-      const int pc = lane % CPR;
-      int s = kb * BN + r;
-      s = s < T ? s : T - 1;     // rows past the end: real (finite) data, masked later
-      const int ck = pc ^ (r & (CPR - 1));
-      const int cv = pc ^ ((4 * (r & 3)) & (CPR - 1));
-      kreg[i] = ld16(kbase + (long long)s * kstride + ck * 8);
-      vreg[i] = ld16(vbase + (long long)s * kstride + cv * 8);
-    }
-  };
-  auto store_block = [&](int st) {
-    bf16* sK = smem + st * 2 * TILE;
-    bf16* sV = sK + TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int span = i * NW + wave;
-      st16(sK + span * 512 + lane * 8, kreg[i]);
-      st16(sV + span * 512 + lane * 8, vreg[i]);
-    }
-  };
-
-  const int key_row = key_row_perm(n);
-  const float sl2 = p.scale_log2;
-  const int q16 = lane >> 4;        // 16-lane group
-  const int j16 = lane & 15;
-
-  load_block(0);
-  store_block(0);
-  __syncthreads();
-  for (int kb = 0; kb < nblocks; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < nblocks) load_block(kb + 1);
-    const bf16* sK = smem + st * 2 * TILE;
-    const bf16* sV = sK + TILE;
-
-    if (wave_active && kb * BN <= tw_max) {
-      float sv[32];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        f32x16 acc = f32x16{};
-        const int r = sub * 32 + key_row;
-        const bf16* krow = sK + r * D;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const int c = (2 * kc + hh) ^ (r & (CPR - 1));
-          acc = mma16(load_frag(krow + c * 8), qf[kc], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[sub * 16 + i] = acc[i] * sl2;
-      }
-      if (kb * BN + BN - 1 > tw_min) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * BN + sub * 32 + reg_key(i, hh) > t_row) sv[sub * 16 + i] = -INFINITY;
-      }
-      online_update_lazy(sv, m_run, l_run, o);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          bf16x8 pf;
-          to_frag(sv + sub * 16 + c * 8, pf);
-          // rows (keys) of the two transposed reads of this lane's 16-lane group
-          const int r0 = sub * 32 + c * 16 + 8 * (q16 >> 1) + (j16 >> 2);
-          const int r1 = r0 + 4;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int chunk = (dt * 4 + 2 * (q16 & 1) + ((j16 & 3) >> 1)) & (CPR - 1);
-            const int half = (j16 & 1) * 4;
-            // r0 & 3 == r1 & 3 == (j16 >> 2)
-            const int pcv = chunk ^ ((4 * (r0 & 3)) & (CPR - 1));
-            const s16x4 lo = lds_read_tr(sV + r0 * D + pcv * 8 + half);
-            const s16x4 hi = lds_read_tr(sV + r1 * D + pcv * 8 + half);
-            const s16x4 a8[2] = {lo, hi};
-            bf16x8 af = *reinterpret_cast<const bf16x8*>(a8);
-            o[dt] = mma16(af, pf, o[dt]);
-          }
-        }
-      }
-    }
-    if (kb + 1 < nblocks) store_block(st ^ 1);
-    __syncthreads();
+  for (int i = 0; i < LOADS; ++i) {
+    const int sp = i * NW + wave;
+    const int r = sp * 4 + lane / 16;
+    const int pc = lane % 16;
+    offk[i] = (uint32_t)(r * (int)kstride + (pc ^ (r & 15)) * 8) * 2u;
+    offv[i] = (uint32_t)(r * (int)kstride + (pc ^ (4 * (r & 3))) * 8) * 2u;
   }
+  const int row_bytes = (int)kstride * 2;
+  // Block blk of one head (K or V) as a raw buffer: rows past the end of the
+  // sequence are out of range and arrive in LDS as zeros.
+  auto block_rsrc = [&](const bf16* head, int blk) {
+    const int valid = T - blk * BN;     // >= 1 for every block that is loaded
+    const int bytes = valid >= BN ? BN * row_bytes : (valid - 1) * row_bytes + D * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(head) + (long long)blk * BN * row_bytes), (short)0, bytes,
+        kBufferWord3);
+  };
+  // load slots [i0, i1) of block blk; slot i covers span i*NW + wave
+  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int i0, int i1) {
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
+#pragma unroll
+    for (int i = i0; i < i1; ++i) dma16(rs, off[i], lbase + (i * NW + wave) * 512);
+  };
+  const int klast = nblocks - 1;
+  auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
+  auto kst = [&](int st) { return smem + st * TILE; };
+  auto vst = [&](int st) { return smem + (2 + st) * TILE; };
+
+  // Lane-constant LDS byte offsets.
+  //  K operand row r = pi(n) of a 32-row half: chunk (2kc + hh) ^ (r & 15);
+  //  pi(n) < 32 and (r & 15) is the same for the second half (rows + 32).
+  const int key_row = key_row_perm(n);
+  uint32_t koff[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    koff[kc] = (uint32_t)(key_row * D + (((2 * kc + hh) ^ (key_row & 15)) * 8)) * 2u;
+  //  V transposed reads: 16-lane group q16, lane j16 reads row
+  //  c16 + 8*(q16/2) + j16/4 (+4), logical chunk 4dt + 2(q16&1) + (j16&3)/2,
+  //  half (j16&1); the swizzle XORs the chunk with 4*(row & 3) = 4*(j16/4).
+  const int q16 = lane >> 4, j16 = lane & 15;
+  const uint32_t smem_base = lds_addr(smem);
+  uint32_t va[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int r = 8 * (q16 >> 1) + (j16 >> 2);
+    const int chunk = (4 * dt + 2 * (q16 & 1) + ((j16 & 3) >> 1)) ^ (4 * (j16 >> 2));
+    va[dt] = smem_base + (uint32_t)(r * D + chunk * 8 + (j16 & 1) * 4) * 2u;
+  }
+  const float sl2 = p.scale_log2;
+
+  // S^T of one 32-key half-block (rows h*32.. of K stage ST) x this wave's 32 rows
+  auto qk = [&]<int ST, int H>(float (&s)[16]) {
+    const char* kb0 = reinterpret_cast<const char*>(smem) + (ST * TILE + H * 32 * D) * 2;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      acc = mma16(*reinterpret_cast<const bf16x8*>(kb0 + koff[kc]), qf[kc], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = acc[i];
+  };
+
+  // Softmax of one 32-key half-block (keys key0 + reg_key(i, hh)): returns the
+  // bf16 probabilities and whether O has to be rescaled by alpha first.
+  auto softmax = [&]<bool MASKED>(float (&s)[16], int key0, bf16x8 (&pf)[2], float& alpha) -> bool {
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[i] = key0 + reg_key(i, hh) > t_row ? -INFINITY : s[i];
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool need = __any(mx > m_run + 8.f);
+    const float m_use = need ? fmaxf(m_run, mx) : m_run;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_use;
+    const float neg_m = -m_use;
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c * 8 + j], sl2, neg_m));
+        sum += e;
+        pf[c][j] = (bf16)e;
+      }
+    }
+    l_run = l_run * alpha + sum;
+    return need;
+  };
+
+  // O += P V over one 32-key half-block H of V stage ST
+  auto pv = [&]<int ST, int H>(const bf16x8 (&pf)[2]) {
+    constexpr int base = ((2 + ST) * TILE + H * 32 * D) * 2;
+    bf16x8 vf[4];
+    tr_read_chunk<base>(va, vf);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[0], o[dt]);
+    tr_read_chunk<base + 16 * D * 2>(va, vf);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[1], o[dt]);
+  };
+
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+  };
+
+  // ---- prologue: K(0) both halves, K(1) first half, V(0) ----
+  dma_rows(kbase, 0, offk, kst(0), 0, LOADS);
+  dma_rows(kbase, clampb(1), offk, kst(1), 0, LOADS / 2);
+  dma_rows(vbase, 0, offv, vst(0), 0, LOADS);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  float s_a[16], s_b[16];
+  qk.template operator()<0, 0>(s_a);
+  __syncthreads();   // every wave has read K(0) rows 0-31 before K(2) overwrites them
+
+  // One 64-key block j (ST = j & 1): half 0 (scores in s_a), half 1 (s_b).
+  //   loads:  K(j+2) rows 0-31 -> K stage ST,   K(j+1) rows 32-63 -> K stage ST^1,
+  //           V(j+1) -> V stage ST^1   (each region was last read before the
+  //           previous barrier)
+  //   half 0: s_b = QK(K(j) rows 32-63) while softmax(s_a); P.V with V(j) rows 0-31
+  //   half 1: s_a = QK(K(j+1) rows 0-31) while softmax(s_b); P.V with V(j) rows 32-63
+  auto block = [&]<bool MASKED, int ST>(int j) {
+    dma_rows(kbase, clampb(j + 2), offk, kst(ST), 0, LOADS / 2);
+    dma_rows(kbase, clampb(j + 1), offk, kst(ST ^ 1), LOADS / 2, LOADS);
+    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, LOADS);
+    bf16x8 pf[2];
+    float alpha;
+    bool need;
+    qk.template operator()<ST, 1>(s_b);
+    need = softmax.template operator()<MASKED>(s_a, j * BN, pf, alpha);
+    if (need) rescale(alpha);
+    pv.template operator()<ST, 0>(pf);
+    qk.template operator()<ST ^ 1, 0>(s_a);
+    need = softmax.template operator()<MASKED>(s_b, j * BN + 32, pf, alpha);
+    if (need) rescale(alpha);
+    pv.template operator()<ST, 1>(pf);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    block.template operator()<false, 0>(j);
+    block.template operator()<false, 1>(j + 1);
+  }
+  if (j < jm) { block.template operator()<false, 0>(j); ++j; }
+  if (j < nblocks && (j & 1)) { block.template operator()<true, 1>(j); ++j; }
+  for (; j + 1 < nblocks; j += 2) {
+    block.template operator()<true, 0>(j);
+    block.template operator()<true, 1>(j + 1);
+  }
+  if (j < nblocks) { block.template operator()<true, 0>(j); ++j; }
 
   // ---- depth fold: this wave's positions only (see moda_fwd.hpp) ----
   if (wave_active && p.L_d > 0) {
@@ -236,7 +322,25 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         const int key = reg_key(i, hh);
         sv[i] = (key >= own_lo && key < own_hi) ? acc[i] * sl2 : -INFINITY;
       }
-      online_update_lazy(sv, m_run, l_run, o);
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+        sum += sv[i];
+      }
+      l_run += sum;
       const bf16* vchunk = vdb + n0 * D;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
