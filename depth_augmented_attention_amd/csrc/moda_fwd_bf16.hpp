@@ -225,13 +225,17 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     m_run = m_use;
     const float neg_m = -m_use;
     float sum = 0.f;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c * 8 + j], sl2, neg_m));
-        sum += e;
-        pf[c][j] = (bf16)e;
+      for (int j = 0; j < 8; ++j)
+        pf[c][j] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[c * 8 + j], sl2, neg_m));
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 pr = {pf[c][j], pf[c][j + 1]};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
       }
     }
     l_run = l_run * alpha + sum;
