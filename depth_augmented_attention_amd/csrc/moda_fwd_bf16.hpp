@@ -18,10 +18,14 @@
 //     V: chunk ^ 4 * (row & 3)), chosen so that every 16-lane K read and every
 //     32-lane transposed V read touches 64 distinct banks.
 //   * At most 256 registers per wave, so two workgroups share a compute unit.
-//   * The running max is only moved (and O rescaled) when a new score exceeds
-//     it by more than 2^8; until then probabilities are taken against the
-//     stale max, which changes nothing in exact arithmetic (out = O / l and
-//     lse = m + log2 l use the same m) and keeps them <= 256.
+//   * Probabilities are taken against the running max without forming the
+//     block's row max first; only when a lane's sum of them exceeds 2^8 (a
+//     score rose well above the max, or the first block) is the row max
+//     formed, the max moved, O rescaled and the probabilities recomputed.
+//     This changes nothing in exact arithmetic (out = O / l and lse =
+//     m + log2 l use the same m), keeps every probability below 2^8, and
+//     drops the max reduction from the common path.  Row sums come from the
+//     same bf16 probabilities that feed the P.V product (v_dot2_f32_bf16).
 //   * The causal mask is only evaluated in the last few blocks of a tile.
 #pragma once
 
@@ -209,24 +213,14 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   // Softmax of one 32-key half-block (keys key0 + reg_key(i, hh)): returns the
   // bf16 probabilities and whether O has to be rescaled by alpha first.
-  auto softmax = [&]<bool MASKED>(float (&s)[16], int key0, bf16x8 (&pf)[2], float& alpha) -> bool {
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        s[i] = key0 + reg_key(i, hh) > t_row ? -INFINITY : s[i];
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    const bool need = __any(mx > m_run + 8.f);
-    const float m_use = need ? fmaxf(m_run, mx) : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_use;
-    const float neg_m = -m_use;
+  // Probabilities are first taken against the current running max; only when
+  // a lane's sum of them exceeds 2^8 (a score rose well above the max, or the
+  // first half) is the row max formed, the max moved, and the probabilities
+  // recomputed.  Exact in real arithmetic either way; keeps them < 2^8.
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  auto exps = [&](const float (&s)[16], float neg_m, bf16x8 (&pf)[2]) {
     float sum = 0.f;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -237,6 +231,27 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         const bf16x2 pr = {pf[c][j], pf[c][j + 1]};
         sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
       }
+    }
+    return sum;
+  };
+  auto softmax = [&]<bool MASKED>(float (&s)[16], int key0, bf16x8 (&pf)[2], float& alpha) -> bool {
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[i] = key0 + reg_key(i, hh) > t_row ? -INFINITY : s[i];
+    }
+    float sum = exps(s, -m_run, pf);
+    const bool need = __any(!(sum <= 256.f));
+    alpha = 1.f;
+    if (need) {
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      const float m_new = fmaxf(m_run, mx);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      sum = exps(s, -m_new, pf);
     }
     l_run = l_run * alpha + sum;
     return need;
