@@ -244,11 +244,13 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     const bool need = __any(!(sum <= 256.f));
     alpha = 1.f;
     if (need) {
+      // only rows whose own max rose by more than 2^8 move it; the others
+      // recompute the same values with alpha = 1 (bit-identical)
       float mx = s[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       sum = exps(s, -m_new, pf);
@@ -346,7 +348,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (__any(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = mx > m_run + 8.f ? mx : m_run;   // per row: bit-stable
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
