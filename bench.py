@@ -49,10 +49,14 @@ def compulsory_bytes(w):
     return eb * (2 * B * T * Hq * d + 2 * B * T * Hkv * d + 2 * B * T * L * Hkv * d) + 4 * B * Hq * T
 
 
+FWD_SOURCES = ("moda_common.hpp", "moda_fwd.hpp", "moda_fwd_bf16.hpp")
+
+
 def kernel_source_hash():
+    """Hash of the sources the fused forward kernel is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "depth_augmented_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FWD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -116,6 +120,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-l0", action="store_true", help="skip the L_d = 0 comparison")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the write-step and depth-window measurements")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
@@ -239,6 +245,40 @@ def main():
         res["overhead_vs_L0"] = avg_fwd / avg_l0 - 1.0
         res["overhead_vs_L0_with_pack"] = (avg_fwd + avg_pack) / avg_l0 - 1.0
         log(f"L_d=0 fwd {avg_l0:.3f} ms, overhead {100 * res['overhead_vs_L0']:.2f}%")
+
+    if not args.no_extras and L_d > 0:
+        # write step: this layer's K/V appended as one slot of the packed buffers
+        log("timing the write step (one slot append) and a depth window")
+        reps = 10
+        ea = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        moda.moda_append_depth(ks, vs, kp, vp, L_d, L_d - 1)
+        torch.cuda.synchronize()
+        ea[0].record()
+        for i in range(reps):
+            moda.moda_append_depth(ks, vs, kp, vp, L_d, L_d - 1)
+            ea[i + 1].record()
+        torch.cuda.synchronize()
+        app_ms = sum(ea[i].elapsed_time(ea[i + 1]) for i in range(reps)) / reps
+        app_bytes = 2 * 2 * ks.numel() * ks.element_size()
+        res["append_ms"] = app_ms
+        res["append_gbps"] = app_bytes / (app_ms * 1e-3) / 1e9
+        res["append_hbm_frac"] = res["append_gbps"] / HBM_PEAK_GBPS
+        # bounded window: the last 8 of the L_d slots
+        lo = max(0, L_d - 8)
+        ew = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        moda.moda_fwd_window(q, ks, vs, kp, vp, L_d, lo, L_d, out=out, lse=lse)
+        torch.cuda.synchronize()
+        ew[0].record()
+        for i in range(3):
+            moda.moda_fwd_window(q, ks, vs, kp, vp, L_d, lo, L_d, out=out, lse=lse)
+            ew[i + 1].record()
+        torch.cuda.synchronize()
+        win_ms = sum(ew[i].elapsed_time(ew[i + 1]) for i in range(3)) / 3
+        res["window_slots"] = [lo, L_d]
+        res["window_fwd_ms"] = win_ms
+        res["window_fwd_tflops"] = (4.0 * B * Hq * d * (T * (T + 1) / 2 + T * (L_d - lo))) / (win_ms * 1e-3) / 1e12
+        if "fwd_ms_L0" in res:
+            res["window_overhead_vs_L0"] = win_ms / res["fwd_ms_L0"] - 1.0
 
     if not args.no_cpu_baseline:
         log(f"oracle on host cores ({args.cpu_budget:.0f} s budget)")

@@ -12,4 +12,10 @@ from ._lib import (  # noqa: F401
     load,
     status_string,
 )
-from .ops import depth_packed_elems, moda_fwd, moda_pack_depth  # noqa: F401
+from .ops import (  # noqa: F401
+    depth_packed_elems,
+    moda_append_depth,
+    moda_fwd,
+    moda_fwd_window,
+    moda_pack_depth,
+)

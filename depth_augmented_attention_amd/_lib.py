@@ -18,7 +18,8 @@ MODA_ERR_UNSUPPORTED = 4
 MODA_ERR_HIP = 5
 
 # every symbol include/moda.h declares
-EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_status_string")
+EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
+           "moda_append_depth", "moda_status_string")
 
 
 class ModaError(RuntimeError):
@@ -47,6 +48,10 @@ def load() -> ctypes.CDLL:
     lib.moda_pack_depth.restype = c_int
     lib.moda_fwd.argtypes = [c_vp] * 6 + [c_vp] + [c_int] * 7 + [c_vp]
     lib.moda_fwd.restype = c_int
+    lib.moda_fwd_window.argtypes = [c_vp] * 6 + [c_vp] + [c_int] * 9 + [c_vp]
+    lib.moda_fwd_window.restype = c_int
+    lib.moda_append_depth.argtypes = [c_vp] * 4 + [c_int] * 7 + [c_vp]
+    lib.moda_append_depth.restype = c_int
     lib.moda_status_string.argtypes = [c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -10,8 +10,10 @@
 
 namespace {
 
-constexpr int kWaves = 4;          // waves per workgroup of the forward kernel
-constexpr int kRowsPerTile = 32 * kWaves;
+constexpr int kWaves = 4;          // waves per workgroup of the forward kernels
+
+// query rows per workgroup of the kernel that serves (dtype, d)
+int rows_per_tile(int, int) { return 32 * kWaves; }
 
 bool valid_dtype(int dtype) { return dtype == MODA_F32 || dtype == MODA_BF16; }
 bool supported_d(int d) { return d == 64 || d == 128; }
@@ -27,6 +29,12 @@ hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D>), dim3(grid), dim3(kWaves * 64), 0, s, p);
   else
     hipLaunchKernelGGL((moda::moda_fwd_kernel<E, D, kWaves>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_append(const moda::AppendParams& p, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((moda::moda_append_depth_kernel<E, D>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -76,27 +84,31 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
-int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
-             const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
-             int L_d, int dtype, void* stream) {
-  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
+                    int L_cap, int slot_lo, int slot_hi, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
+  if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
   if (!q || !k_seq || !v_seq || !out) return MODA_ERR_NULL;
+  const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
-  const long long ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
+  const int tile_rows = rows_per_tile(dtype, d);
+  const long long ntiles = (rows + tile_rows - 1) / tile_rows;
   const long long grid = ntiles * B * Hkv;
   if (grid > 0x7fffffffLL || rows > 0x7fffffffLL) return MODA_ERR_SHAPE;
 
   moda::FwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
   p.out = out; p.lse = lse;
-  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.L_d = L_d;
+  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
+  p.L_d = L_d; p.L_cap = L_cap > 0 ? L_cap : 1; p.slot_lo = slot_lo;
   p.ntiles = (int)ntiles;
-  p.NKp = padded_depth_keys(T, L_d);
+  p.NKp = padded_depth_keys(T, L_cap);
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -105,6 +117,35 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
     e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)grid, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, s);
   else
     e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, s) : launch_fwd<float, 64>(p, (unsigned)grid, s);
+  return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+             const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
+             int L_d, int dtype, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return moda_fwd_window(q, k_seq, v_seq, k_depth, v_depth, out, lse, B, T, Hq, Hkv, d, L_d, 0, L_d,
+                         dtype, stream);
+}
+
+int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void* v_packed, int B,
+                      int T, int Hkv, int d, int L_cap, int slot, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_cap < 1) return MODA_ERR_SHAPE;
+  if (slot < 0 || slot >= L_cap) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !k_packed || !v_packed) return MODA_ERR_NULL;
+  moda::AppendParams p{k_new, v_new, k_packed, v_packed, B, T, Hkv, L_cap, slot, padded_depth_keys(T, L_cap)};
+  const int ve = dtype == MODA_BF16 ? 8 : 4;
+  const long long threads = (long long)B * T * Hkv * (d / ve);
+  const long long grid = (threads + 255) / 256;
+  if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == MODA_BF16)
+    e = d == 128 ? launch_append<moda::bf16, 128>(p, (unsigned)grid, s) : launch_append<moda::bf16, 64>(p, (unsigned)grid, s);
+  else
+    e = d == 128 ? launch_append<float, 128>(p, (unsigned)grid, s) : launch_append<float, 64>(p, (unsigned)grid, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 

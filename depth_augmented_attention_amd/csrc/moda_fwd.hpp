@@ -37,17 +37,31 @@ struct FwdParams {
   const void* vd;   // packed depth values [B][Hkv][NKp/32][D][32]
   void* out;
   float* lse;
-  int B, T, Hq, Hkv, G, L_d;
+  int B, T, Hq, Hkv, G;
+  int L_d;          // depth slots read per position (slot_lo .. slot_lo+L_d-1)
+  int L_cap;        // slots per position in the packed buffers (key n = t*L_cap + slot)
+  int slot_lo;      // first slot read
   int ntiles;       // query tiles per (b, kvh)
   long long NKp;    // padded depth keys per (b, kvh)
   float scale_log2; // log2(e) / sqrt(d)
 };
 
+// Whether the 32 packed depth keys [n0, n0 + 32) hold any slot of the window
+// [slot_lo, slot_lo + L_d) of some position (a tile inside one position that
+// misses the window is skipped; tiles spanning several positions are kept).
+__device__ __forceinline__ bool depth_tile_used(long long n0, int L_cap, int slot_lo, int L_d) {
+  const long long t0 = n0 / L_cap, t1 = (n0 + 31) / L_cap;
+  if (t0 != t1) return true;
+  const long long w0 = t0 * L_cap + slot_lo;
+  return w0 < n0 + 32 && w0 + L_d > n0;
+}
+
 // Online-softmax step over NV new scores (log2 units, masked ones -inf) held
 // by this lane for its query; the other lane half holds the rest of the
 // block.  Updates the running max m and sum l, rescales O^T, and turns sv
-// into unnormalised probabilities 2^(s - m).
-template <int NV, int NDT>
+// into unnormalised probabilities 2^(s - m), rounded to the element type E
+// that enters the P.V product, so that l sums exactly the weights applied.
+template <typename E, int NV, int NDT>
 __device__ __forceinline__ void online_update(float (&sv)[NV], float& m_run, float& l_run,
                                               f32x16 (&o)[NDT]) {
   float mx = sv[0];
@@ -59,7 +73,7 @@ __device__ __forceinline__ void online_update(float (&sv)[NV], float& m_run, flo
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+    sv[i] = (float)(E)__builtin_amdgcn_exp2f(sv[i] - m_new);
     sum += sv[i];
   }
   l_run = l_run * alpha + sum;
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
           for (int r = 0; r < 16; ++r)
             if (kb * BN + st * 32 + reg_key(r, hh) > t_row) sv[st * 16 + r] = -INFINITY;
       }
-      online_update(sv, m_run, l_run, o);
+      online_update<E>(sv, m_run, l_run, o);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -240,25 +254,26 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
 
   // ---- depth fold: this wave's positions only ----
   if (wave_active && p.L_d > 0) {
-    const int L_d = p.L_d;
-    const long long nlo = (long long)tw_min * L_d;
-    const long long nhi = (long long)(tw_max + 1) * L_d;
+    const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+    const long long nlo = (long long)tw_min * L_cap + slot_lo;
+    const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
     const E* kdb = reinterpret_cast<const E*>(p.kd) + (long long)bh * p.NKp * D;
     const E* vdb = reinterpret_cast<const E*>(p.vd) + (long long)bh * p.NKp * D;
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+      if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
       const E* krow = kdb + (n0 + key_row) * D + hh * 8;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
       float sv[16];
-      const long long own_lo = (long long)t_row * L_d - n0;   // this row's slots,
-      const long long own_hi = own_lo + L_d;                  // relative to n0
+      const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;   // this row's slots,
+      const long long own_hi = own_lo + L_d;                              // relative to n0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = reg_key(r, hh);
         sv[r] = (key >= own_lo && key < own_hi) ? acc[r] * sl2 : -INFINITY;
       }
-      online_update(sv, m_run, l_run, o);
+      online_update<E>(sv, m_run, l_run, o);
       const E* vchunk = vdb + n0 * D;   // [D][32] block of this 32-key chunk
 #pragma unroll
       for (int c = 0; c < 2; ++c) {

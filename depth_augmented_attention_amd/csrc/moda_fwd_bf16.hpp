@@ -325,52 +325,47 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   // ---- depth fold: this wave's positions only (see moda_fwd.hpp) ----
   if (wave_active && p.L_d > 0) {
-    const int L_d = p.L_d;
-    const long long nlo = (long long)tw_min * L_d;
-    const long long nhi = (long long)(tw_max + 1) * L_d;
+    const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+    const long long nlo = (long long)tw_min * L_cap + slot_lo;
+    const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
     const bf16* kdb = reinterpret_cast<const bf16*>(p.kd) + (long long)bh * p.NKp * D;
     const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+      if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
       const bf16* krow = kdb + (n0 + key_row) * D + hh * 8;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+      // same arithmetic as a sequence half-block: masked raw scores, one FMA
+      // into exp2; the max is exact here (these tiles are few) and the sum is
+      // taken over the bf16-rounded probabilities that enter P.V
       float sv[16];
-      const long long own_lo = (long long)t_row * L_d - n0;
+      const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
       const long long own_hi = own_lo + L_d;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = reg_key(i, hh);
-        sv[i] = (key >= own_lo && key < own_hi) ? acc[i] * sl2 : -INFINITY;
+        sv[i] = (key >= own_lo && key < own_hi) ? acc[i] : -INFINITY;
       }
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_run + 8.f)) {
-        const float m_new = mx > m_run + 8.f ? mx : m_run;   // per row: bit-stable
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      if (__any(mx > m_run)) {
+        const float m_new = fmaxf(mx, m_run);   // per row: alpha == 1 where it stays
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        rescale(alpha);
         m_run = m_new;
       }
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
-        sum += sv[i];
-      }
-      l_run += sum;
+      bf16x8 pf[2];
+      l_run += exps(sv, -m_run, pf);
       const bf16* vchunk = vdb + n0 * D;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 pf;
-        to_frag(sv + c * 8, pf);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = mma16(load_frag(vchunk + (dt * 32 + n) * 32 + c * 16 + hh * 8), pf, o[dt]);
-      }
+          o[dt] = mma16(load_frag(vchunk + (dt * 32 + n) * 32 + c * 16 + hh * 8), pf[c], o[dt]);
     }
   }
 

@@ -72,3 +72,51 @@ __global__ __launch_bounds__(256) void moda_pack_depth_kernel(PackParams p) {
 }
 
 }  // namespace moda
+
+namespace moda {
+
+// Write step: one layer's K/V of every position into one slot of the packed
+// depth buffers (the layer appends its KV to the depth stream that later
+// layers read -- gist.science (de) "Mixture-of-Depths Attention", Technische
+// Zusammenfassung section 2, Write-Step).  Same packed layout as
+// moda_pack_depth_kernel with L_cap slots per position:
+//   k_packed[b][kvh][t * L_cap + slot][:]   = k_new[b][t][kvh][:]
+//   v_packed[b][kvh][n / 32][e][n % 32]      = v_new[b][t][kvh][e],  n = t * L_cap + slot
+// One thread per 16-byte chunk of one (b, t, kvh) row: the key chunk is one
+// 16-byte store, the value chunk VE strided element stores.
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* kp;
+  void* vp;
+  int B, T, Hkv, L_cap, slot;
+  long long NKp;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_append_depth_kernel(AppendParams p) {
+  constexpr int VE = Traits<E>::VE;
+  constexpr int CPR = D / VE;     // 16-byte chunks per row
+  const long long rows = (long long)p.B * p.T * p.Hkv;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * CPR) return;
+  const long long row = idx / CPR;              // (b, t, kvh) in input order
+  const int c = (int)(idx % CPR);
+  const int kvh = (int)(row % p.Hkv);
+  const long long bt = row / p.Hkv;
+  const int t = (int)(bt % p.T);
+  const int b = (int)(bt / p.T);
+  const long long bh = (long long)b * p.Hkv + kvh;
+  const long long n = (long long)t * p.L_cap + p.slot;
+  const E* ks = reinterpret_cast<const E*>(p.k_new) + row * D + c * VE;
+  const E* vs = reinterpret_cast<const E*>(p.v_new) + row * D + c * VE;
+  E* kd = reinterpret_cast<E*>(p.kp) + (bh * p.NKp + n) * D + c * VE;
+  st16(kd, ld16(ks));
+  E vals[VE];
+  *reinterpret_cast<u32x4*>(vals) = ld16(vs);
+  E* vd = reinterpret_cast<E*>(p.vp) + bh * p.NKp * D + (n / 32) * D * 32 + (n % 32);
+#pragma unroll
+  for (int e = 0; e < VE; ++e) vd[(c * VE + e) * 32] = vals[e];
+}
+
+}  // namespace moda

@@ -69,12 +69,46 @@ def moda_pack_depth(k_depth: torch.Tensor, v_depth: torch.Tensor,
     return k_packed, v_packed
 
 
+def moda_append_depth(k_new: torch.Tensor, v_new: torch.Tensor, k_packed: torch.Tensor,
+                      v_packed: torch.Tensor, L_cap: int, slot: int, stream=None):
+    """Write step: store this layer's K/V [B,T,Hkv,d] into slot `slot` of packed
+    depth buffers with L_cap slots per position (in place)."""
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must both be [B,T,Hkv,d] of one dtype")
+    B, T, Hkv, d = k_new.shape
+    n = depth_packed_elems(B, T, Hkv, d, L_cap)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k_packed, "k_packed"), (v_packed, "v_packed")):
+        _dev(t, name)
+    if k_packed.numel() != n or v_packed.numel() != n or k_packed.dtype != k_new.dtype \
+            or v_packed.dtype != k_new.dtype:
+        raise ValueError(f"packed buffers must hold {n} elements of {k_new.dtype}")
+    st = load().moda_append_depth(k_new.data_ptr(), v_new.data_ptr(), k_packed.data_ptr(),
+                                  v_packed.data_ptr(), B, T, Hkv, d, L_cap, slot,
+                                  _dtype_code(k_new), _stream(stream))
+    check(st, "moda_append_depth")
+    return k_packed, v_packed
+
+
 def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
              k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
              with_lse: bool = True, stream=None):
     """MoDA forward.  q [B,T,Hq,d]; k_seq, v_seq [B,T,Hkv,d]; k_depth, v_depth
     are the packed buffers from moda_pack_depth (None when L_d == 0).
+
+    Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
+    """
+    return moda_fwd_window(q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out=out, lse=lse,
+                           with_lse=with_lse, stream=stream)
+
+
+def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+                    k_depth: torch.Tensor | None, v_depth: torch.Tensor | None,
+                    L_cap: int, slot_lo: int, slot_hi: int,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                    with_lse: bool = True, stream=None):
+    """MoDA forward reading depth slots [slot_lo, slot_hi) of packed buffers
+    with L_cap slots per position.
 
     Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
     """
@@ -89,10 +123,10 @@ def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq")):
         _dev(t, name)
     kd_ptr = vd_ptr = None
-    if L_d > 0:
+    if slot_hi > slot_lo:
         if k_depth is None or v_depth is None:
-            raise ValueError("packed depth buffers are required when L_d > 0")
-        n = depth_packed_elems(B, T, Hkv, d, L_d)
+            raise ValueError("packed depth buffers are required when slots are read")
+        n = depth_packed_elems(B, T, Hkv, d, L_cap)
         for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
             _dev(t, name)
             if t.numel() != n or t.dtype != q.dtype:
@@ -107,8 +141,9 @@ def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
-    st = load().moda_fwd(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
-                         out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                         B, T, Hq, Hkv, d, L_d, _dtype_code(q), _stream(stream))
-    check(st, "moda_fwd")
+    st = load().moda_fwd_window(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+                                out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, _dtype_code(q),
+                                _stream(stream))
+    check(st, "moda_fwd_window")
     return out, lse

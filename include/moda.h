@@ -116,6 +116,56 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
              int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
              void* stream);
 
+/*
+ * moda_fwd_window -- fused forward over a window of depth slots.
+ *
+ * The depth stream can hold more slots than one layer reads: a buffer packed
+ * with L_cap slots per position (by moda_pack_depth with L_d = L_cap, or by
+ * moda_append_depth), of which this call reads slots slot_lo .. slot_hi-1 of
+ * each position.  This is the bounded depth-KV slot cache (sliding window or
+ * selected range) that gist.science (de) "Mixture-of-Depths Attention",
+ * Technische Zusammenfassung section 5, proposes for very deep models, and the
+ * read side of the write step below (layer l reads slots 0 .. l-1).
+ *
+ *   k_depth, v_depth : packed buffers with L_cap slots per position, i.e.
+ *                      moda_depth_packed_elems(B, T, Hkv, d, L_cap) elements
+ *                      each; every slot must hold finite values (zero-fill
+ *                      a buffer before appending into it); NULL allowed iff
+ *                      slot_lo == slot_hi
+ *   L_cap            : slots per position in the packed buffers (>= 0)
+ *   slot_lo, slot_hi : 0 <= slot_lo <= slot_hi <= L_cap
+ *   all other arguments as for moda_fwd.
+ *
+ * moda_fwd(..., L_d, ...) is moda_fwd_window(..., L_cap = L_d, 0, L_d, ...).
+ */
+int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq,
+                    const void* k_depth, const void* v_depth,
+                    void* out, float* lse,
+                    int B, int T, int Hq, int Hkv, int d,
+                    int L_cap, int slot_lo, int slot_hi, int dtype,
+                    void* stream);
+
+/*
+ * moda_append_depth -- the write step: store one layer's K/V of every
+ * position into slot `slot` of packed depth buffers with L_cap slots per
+ * position (gist.science (de) "Mixture-of-Depths Attention", Technische
+ * Zusammenfassung section 2, Write-Step: a layer appends its KV pairs to the
+ * depth stream that later layers read).
+ *
+ *   k_new, v_new     : in,  [B, T, Hkv, d] dtype (this layer's keys / values)
+ *   k_packed, v_packed : in/out, packed buffers of
+ *                      moda_depth_packed_elems(B, T, Hkv, d, L_cap) elements;
+ *                      only the entries of slot `slot` are written
+ *   0 <= slot < L_cap.
+ *
+ * Appending slots 0 .. L-1 in turn into zero-filled buffers gives exactly the
+ * bytes that moda_pack_depth produces for the same L = L_cap slots.
+ */
+int moda_append_depth(const void* k_new, const void* v_new,
+                      void* k_packed, void* v_packed,
+                      int B, int T, int Hkv, int d, int L_cap, int slot, int dtype,
+                      void* stream);
+
 /* Static, human-readable name of a moda_status value. */
 const char* moda_status_string(int status);
 

@@ -96,3 +96,25 @@ def test_product_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 src = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in src.lower(), f"{f} mentions the oracle"
+
+
+def test_window_validation():
+    lib = moda.load()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 1, 128)
+    assert lib.moda_fwd_window(*args, 4, 0, 5, 1, None) == _lib.MODA_ERR_SHAPE    # hi > L_cap
+    assert lib.moda_fwd_window(*args, 4, 3, 2, 1, None) == _lib.MODA_ERR_SHAPE    # lo > hi
+    assert lib.moda_fwd_window(*args, 4, -1, 2, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_fwd_window(*args, -1, 0, 0, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_fwd_window(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 4, 2, 1, 128,
+                               4, 1, 2, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_fwd_window(*args, 4, 0, 2, 9, None) == _lib.MODA_ERR_DTYPE
+
+
+def test_append_validation():
+    lib = moda.load()
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 3, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 0, 0, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, -1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth(None, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 1, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 96, 3, 1, 1, None) == _lib.MODA_ERR_UNSUPPORTED
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 1, 4, None) == _lib.MODA_ERR_DTYPE
