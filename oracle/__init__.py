@@ -1,4 +1,4 @@
-"""Reference (oracle) implementation of the MoDA forward pass.
+"""Reference (oracle) implementation of the MoDA forward pass and its gradients.
 
 Test infrastructure only: imported by the tests, by the smoke check and by the
 CPU-baseline leg of the benchmark, never by the product path.
@@ -8,3 +8,4 @@ from .moda_oracle import (  # noqa: F401
     moda_forward_scalar,
     depth_utilisation,
 )
+from .moda_backward import moda_backward  # noqa: F401

@@ -1,0 +1,58 @@
+"""CPU pins of the backward oracle, and planted mistakes that they must catch."""
+import os
+import types
+
+import pytest
+
+import oracle_bwd_pins
+from oracle import moda_backward
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "moda_backward.py")
+
+
+@pytest.mark.parametrize("name", sorted(oracle_bwd_pins.BWD_PINS))
+def test_backward_pin(name):
+    worst = oracle_bwd_pins.BWD_PINS[name](moda_backward)
+    print(f"{name}: worst deviation {worst:.3e}")
+
+
+# Each mutant is a copy of oracle/moda_backward.py with one plausible slip;
+# it must fail a pin other than the per-group consistency check.
+MUTANTS = {
+    "no_jacobian_term": [("dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "dz = p * dp")],
+    "jacobian_sign": [("dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+                       "dz = p * (dp + (p * dp).sum(axis=1, keepdims=True))")],
+    "dq_unscaled": [("dQ = (dz @ Kc) * scale", "dQ = dz @ Kc")],
+    "dk_unscaled": [("dK = (dz.T @ Qg) * scale", "dK = dz.T @ Qg")],
+    "dk_uses_dout": [("dK = (dz.T @ Qg) * scale", "dK = (dz.T @ dOg) * scale")],
+    "dv_unnormalised": [("dV = p.T @ dOg", "dV = e.T @ dOg")],
+    "dp_uses_keys": [("dp = dOg @ Vc.T", "dp = dOg @ Kc.T")],
+    "depth_grad_prev_position": [("dkd[b, t, :, kvh] = gkd", "dkd[b, max(t - 1, 0), :, kvh] += gkd")],
+    "seq_grad_excludes_self": [("dks[b, kvh, : t + 1] += gks", "dks[b, kvh, : t] += gks[:t]")],
+    "gqa_first_head_only": [("heads = slice(kvh * G, (kvh + 1) * G)", "heads = slice(kvh * G, kvh * G + 1)")],
+    "scale_1_over_d": [("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d")],
+}
+
+
+def _mutant(edits):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("moda_backward_mutant")
+    exec(compile(src, "moda_backward_mutant", "exec"), mod.__dict__)
+    return mod.moda_backward
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_backward_mutant_is_caught(name):
+    bwd = _mutant(MUTANTS[name])
+    caught = []
+    for pname, pin in oracle_bwd_pins.BWD_PINS.items():
+        if pname == "groups":
+            continue
+        try:
+            pin(bwd)
+        except Exception:
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every pin"
