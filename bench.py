@@ -122,6 +122,7 @@ def main():
     ap.add_argument("--no-l0", action="store_true", help="skip the L_d = 0 comparison")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the write-step and depth-window measurements")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
@@ -279,6 +280,31 @@ def main():
         res["window_fwd_tflops"] = (4.0 * B * Hq * d * (T * (T + 1) / 2 + T * (L_d - lo))) / (win_ms * 1e-3) / 1e12
         if "fwd_ms_L0" in res:
             res["window_overhead_vs_L0"] = win_ms / res["fwd_ms_L0"] - 1.0
+
+    if not args.no_bwd:
+        # backward of the same forward: dq, dk/dv of sequence and depth keys
+        from moda_inputs import make_dout
+        log("timing the backward (moda_bwd)")
+        moda.moda_fwd(q, ks, vs, kp, vp, L_d, out=out, lse=lse)
+        dout = make_dout(B, T, Hq, d, dtype=w["dtype"], seed=w["seed"]).to(q.device)
+        grads = moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout)
+        torch.cuda.synchronize()
+        reps = 3
+        eb = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        eb[0].record()
+        for i in range(reps):
+            moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout, grads=grads)
+            eb[i + 1].record()
+        torch.cuda.synchronize()
+        bwd_ms = sum(eb[i].elapsed_time(eb[i + 1]) for i in range(reps)) / reps
+        # useful work: five products over the unmasked scores (S recomputed,
+        # dP, dV, dQ, dK), 2.5x the forward's two; the kernels execute seven
+        # (S and dP are formed once for dq and once for dk/dv)
+        res["bwd_ms"] = bwd_ms
+        res["bwd_tflops"] = 2.5 * F / (bwd_ms * 1e-3) / 1e12
+        res["bwd_frac_mfma_peak"] = res["bwd_tflops"] / peak
+        log(f"bwd {bwd_ms:.3f} ms  {res['bwd_tflops']:.1f} TFLOP/s")
+        del grads, dout
 
     if not args.no_cpu_baseline:
         log(f"oracle on host cores ({args.cpu_budget:.0f} s budget)")

@@ -1,4 +1,4 @@
-"""MoDA (mixture-of-depths attention) forward for AMD Instinct MI355X (gfx950).
+"""MoDA (mixture-of-depths attention) forward and backward for AMD Instinct MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind the C ABI of
 libmoda.so (include/moda.h); this package only marshals tensors into it.
@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     depth_packed_elems,
     moda_append_depth,
+    moda_bwd,
     moda_fwd,
     moda_fwd_window,
     moda_pack_depth,

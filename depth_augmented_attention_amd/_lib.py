@@ -19,7 +19,7 @@ MODA_ERR_HIP = 5
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
-           "moda_append_depth", "moda_status_string")
+           "moda_append_depth", "moda_bwd", "moda_status_string")
 
 
 class ModaError(RuntimeError):
@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.moda_fwd_window.restype = c_int
     lib.moda_append_depth.argtypes = [c_vp] * 4 + [c_int] * 7 + [c_vp]
     lib.moda_append_depth.restype = c_int
+    lib.moda_bwd.argtypes = [c_vp] * 14 + [c_int] * 7 + [c_vp]
+    lib.moda_bwd.restype = c_int
     lib.moda_status_string.argtypes = [c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include "moda.h"
+#include "moda_bwd.hpp"
 #include "moda_fwd.hpp"
 #include "moda_fwd_bf16.hpp"
 #include "moda_pack.hpp"
@@ -41,6 +42,20 @@ hipError_t launch_append(const moda::AppendParams& p, unsigned grid, hipStream_t
 template <typename E, int D>
 hipError_t launch_pack(const moda::PackParams& p, unsigned grid, hipStream_t s) {
   hipLaunchKernelGGL((moda::moda_pack_depth_kernel<E, D>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
+  constexpr int ve = 16 / sizeof(E);
+  const long long rows = (long long)p.B * p.T * p.Hq;
+  const long long rpb = 256 / (D / ve);
+  hipLaunchKernelGGL((moda::moda_bwd_delta_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
+  const unsigned BH = (unsigned)(p.B * p.Hkv);
+  hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+  if (p.L_d > 0)
+    hipLaunchKernelGGL((moda::moda_bwd_depth_kernel<E, D>), dim3((unsigned)((long long)p.T * BH)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -146,6 +161,47 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
     e = d == 128 ? launch_append<moda::bf16, 128>(p, (unsigned)grid, s) : launch_append<moda::bf16, 64>(p, (unsigned)grid, s);
   else
     e = d == 128 ? launch_append<float, 128>(p, (unsigned)grid, s) : launch_append<float, 64>(p, (unsigned)grid, s);
+  return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+             const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+             void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* delta, int B, int T,
+             int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || !delta)
+    return MODA_ERR_NULL;
+  if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
+  const int G = Hq / Hkv;
+  const long long rows = (long long)T * G;
+  const long long ntiles = (rows + 32 * kWaves - 1) / (32 * kWaves);
+  const long long nktiles = ((long long)T + 32 * kWaves - 1) / (32 * kWaves);
+  const long long BH = (long long)B * Hkv;
+  if (ntiles * BH > 0x7fffffffLL || (long long)T * BH > 0x7fffffffLL || rows > 0x7fffffffLL ||
+      (long long)B * T * Hq > 0x7fffffffLL * 4)
+    return MODA_ERR_SHAPE;
+
+  moda::BwdParams p;
+  p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
+  p.o = out; p.dO = dout; p.lse = lse; p.delta = delta;
+  p.dq = dq; p.dk = dk_seq; p.dv = dv_seq; p.dkd = dk_depth; p.dvd = dv_depth;
+  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
+  p.L_d = L_d; p.L_cap = L_d > 0 ? L_d : 1; p.slot_lo = 0;
+  p.ntiles = (int)ntiles;
+  p.nktiles = (int)nktiles;
+  p.NKp = padded_depth_keys(T, L_d);
+  p.scale = (float)(1.0 / sqrt((double)d));
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == MODA_BF16)
+    e = d == 128 ? launch_bwd<moda::bf16, 128>(p, s) : launch_bwd<moda::bf16, 64>(p, s);
+  else
+    e = d == 128 ? launch_bwd<float, 128>(p, s) : launch_bwd<float, 64>(p, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 

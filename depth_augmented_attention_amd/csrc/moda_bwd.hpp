@@ -1,0 +1,610 @@
+// MoDA backward kernels for gfx950.
+//
+// The forward is one softmax over the causal sequence keys s <= t of the
+// current layer joined with the depth slots of the same position t (mhpn.cn
+// article "动态混合深度注意力机制MoDA技术解析", section 1.2 formula and section
+// 2.2 masks).  Its gradients, for dO = dL/dout, with z the scaled scores,
+// P = exp(z - lse) the probabilities the forward used and
+// Delta = rowsum(dO * out) (the softmax Jacobian term sum_j P_j dP_j):
+//   dV_j = sum_i P_ij dO_i          dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - Delta_i)  dQ_i = scale sum_j dS_ij k_j
+//   dK_j = scale sum_i dS_ij q_i
+// Four kernels, all on the caller's stream in this order:
+//   moda_bwd_delta_kernel  Delta [B,Hq,T] from out and dO.
+//   moda_bwd_dq_kernel     one workgroup per query tile (rows fold GQA as in
+//                          the forward: row R is position R / G, head
+//                          kvh*G + R % G); sweeps the causal key blocks like
+//                          the forward, recomputing P from lse, and folds in
+//                          the row's own depth slots; writes dq.
+//   moda_bwd_dkdv_kernel   one workgroup per 128 sequence keys of one
+//                          (b, kv head); sweeps every query row at or after
+//                          the keys' positions (all G heads); writes dk_seq,
+//                          dv_seq.  No atomics: each key has one writer.
+//   moda_bwd_depth_kernel  one workgroup per (b, t, kv head): the depth slots
+//                          of position t are seen only by the G heads at t
+//                          (the depth mask), so their gradients are local to
+//                          that group; writes dk_depth, dv_depth in the
+//                          logical [B,T,L_d,Hkv,d] layout.
+// The products run on the matrix cores with float32 accumulation in the
+// transposed orientation of the forward (a lane owns one query, or one key);
+// probabilities and dS enter them in the input precision.
+#pragma once
+
+#include "moda_common.hpp"
+#include "moda_fwd.hpp"   // depth_tile_used
+
+namespace moda {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kd;      // packed depth keys   [B][Hkv][NKp][D]
+  const void* vd;      // packed depth values [B][Hkv][NKp/32][D][32]
+  const void* o;       // forward output [B,T,Hq,D]
+  const void* dO;      // gradient of the output [B,T,Hq,D]
+  const float* lse;    // forward lse [B,Hq,T] (natural log)
+  float* delta;        // [B,Hq,T], written by the first kernel
+  void* dq;            // [B,T,Hq,D]
+  void* dk;            // [B,T,Hkv,D]
+  void* dv;
+  void* dkd;           // [B,T,L_d,Hkv,D]
+  void* dvd;
+  int B, T, Hq, Hkv, G;
+  int L_d, L_cap, slot_lo;
+  int ntiles;          // query tiles per (b, kvh)
+  int nktiles;         // key tiles per (b, kvh)
+  long long NKp;
+  float scale;         // 1 / sqrt(d)
+  float scale_log2;    // log2(e) / sqrt(d)
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Four rows x VE elements (v[r] = VE consecutive elements of row row0 + r,
+// starting at element e0) written transposed: sT[(e0 + e) * LDT + row0 + r].
+template <typename E, int LDT>
+__device__ __forceinline__ void store_t4(E* sT, int e0, int row0, const u32x4 (&v)[4]) {
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t sel = s ? 0x07060302u : 0x05040100u;
+        u32x2 val;
+        val[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+        val[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+        *reinterpret_cast<u32x2*>(sT + (e0 + 2 * w + s) * LDT + row0) = val;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u32x4 val = {v[0][e], v[1][e], v[2][e], v[3][e]};
+      st16(sT + (e0 + e) * LDT + row0, val);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO * out), one 16-byte chunk per thread.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_bwd_delta_kernel(BwdParams p) {
+  constexpr int VE = Traits<E>::VE;
+  constexpr int CPR = D / VE;         // chunks per row (8 or 16)
+  constexpr int RPB = 256 / CPR;      // rows per workgroup
+  const long long rows = (long long)p.B * p.T * p.Hq;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CPR;
+  const int c = threadIdx.x % CPR;
+  float s = 0.f;
+  if (row < rows) {
+    E o[VE], g[VE];
+    *reinterpret_cast<u32x4*>(o) = ld16(reinterpret_cast<const E*>(p.o) + row * D + c * VE);
+    *reinterpret_cast<u32x4*>(g) = ld16(reinterpret_cast<const E*>(p.dO) + row * D + c * VE);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) s += (float)o[e] * (float)g[e];
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (row < rows && c == 0) {
+    const int h = (int)(row % p.Hq);
+    const long long bt = row / p.Hq;
+    const int t = (int)(bt % p.T);
+    const int b = (int)(bt / p.T);
+    p.delta[((long long)b * p.Hq + h) * p.T + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: per query tile, S^T = K Q^T and dP^T = V dO^T per 32-key half, then
+// dQ^T += K^T dS^T.  K is staged key-major (score operand) and transposed
+// (dQ operand); V key-major.
+template <typename E, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
+  using Frag = typename Traits<E>::Frag;
+  constexpr int BN = 64;
+  constexpr int VE = Traits<E>::VE;
+  constexpr int KLD = D + VE;          // key-major row stride (16 B pad)
+  constexpr int TLD = BN + VE;         // transposed row stride (16 B pad)
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int NU = BN * D / (4 * VE);   // units of 4 rows x 16 bytes per block
+  constexpr int UPT = (NU + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) E sK[BN * KLD];
+  __shared__ __attribute__((aligned(16))) E sV[BN * KLD];
+  __shared__ __attribute__((aligned(16))) E sKt[D * TLD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int tile = p.ntiles - 1 - (int)(blockIdx.x / BH);   // heaviest first
+  const int b = bh / p.Hkv;
+  const int kvh = bh % p.Hkv;
+  const int G = p.G;
+  const int T = p.T;
+  const long long TG = (long long)T * G;
+
+  const long long R0 = (long long)tile * (NW * 32);
+  const long long Rw = R0 + wave * 32;
+  const long long R = Rw + n;
+  const bool row_ok = R < TG;
+  const bool wave_active = Rw < TG;
+  const int t_row = row_ok ? (int)(R / G) : T - 1;
+  const int hq = kvh * G + (row_ok ? (int)(R % G) : 0);
+  const int tw_min = wave_active ? (int)(Rw / G) : T - 1;
+  const int tw_max = wave_active ? (int)((Rw + 31 < TG ? Rw + 31 : TG - 1) / G) : T - 1;
+  const long long Rlast = (R0 + NW * 32 < TG ? R0 + NW * 32 : TG) - 1;
+  const int nblocks = (int)(Rlast / G) / BN + 1;
+
+  const long long qrow = (((long long)b * T + t_row) * p.Hq + hq) * D + hh * 8;
+  Frag qf[NKC], df[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    qf[kc] = row_ok ? load_frag(reinterpret_cast<const E*>(p.q) + qrow + kc * 16) : zero_frag<Frag>();
+    df[kc] = row_ok ? load_frag(reinterpret_cast<const E*>(p.dO) + qrow + kc * 16) : zero_frag<Frag>();
+  }
+  const long long lrow = ((long long)b * p.Hq + hq) * T + t_row;
+  const float lse2 = row_ok ? p.lse[lrow] * kLog2e : INFINITY;   // P = 0 on rows past the end
+  const float dlt = row_ok ? p.delta[lrow] : 0.f;
+  const float sl2 = p.scale_log2;
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
+
+  const long long kstride = (long long)p.Hkv * D;
+  const E* kbase = reinterpret_cast<const E*>(p.k) + ((long long)b * T * p.Hkv + kvh) * D;
+  const E* vbase = reinterpret_cast<const E*>(p.v) + ((long long)b * T * p.Hkv + kvh) * D;
+
+  u32x4 kreg[UPT][4], vreg[UPT][4];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      const int rg = u % (BN / 4), dc = u / (BN / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = kb * BN + rg * 4 + r;
+        const bool ok = u < NU && s < T;
+        kreg[i][r] = ok ? ld16(kbase + (long long)s * kstride + dc * VE) : u32x4{0, 0, 0, 0};
+        vreg[i][r] = ok ? ld16(vbase + (long long)s * kstride + dc * VE) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      if (u >= NU) continue;
+      const int rg = u % (BN / 4), dc = u / (BN / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st16(sK + (rg * 4 + r) * KLD + dc * VE, kreg[i][r]);
+        st16(sV + (rg * 4 + r) * KLD + dc * VE, vreg[i][r]);
+      }
+      store_t4<E, TLD>(sKt, dc * VE, rg * 4, kreg[i]);
+    }
+  };
+
+  const int key_row = key_row_perm(n);
+
+  load_block(0);
+  for (int kb = 0; kb < nblocks; ++kb) {
+    __syncthreads();
+    store_block();
+    __syncthreads();
+    if (kb + 1 < nblocks) load_block(kb + 1);
+    if (!(wave_active && kb * BN <= tw_max)) continue;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const E* krow = sK + (st * 32 + key_row) * KLD + hh * 8;
+      const E* vrow = sV + (st * 32 + key_row) * KLD + hh * 8;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mma16(load_frag(krow + kc * 16), qf[kc], s);
+        dp = mma16(load_frag(vrow + kc * 16), df[kc], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * BN + st * 32 + reg_key(r, hh);
+        const float pr = key <= t_row ? __builtin_amdgcn_exp2f(s[r] * sl2 - lse2) : 0.f;
+        ds[r] = pr * (dp[r] - dlt);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag f;
+        to_frag(ds + c * 8, f);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          acc[dt] = mma16(load_frag(sKt + (dt * 32 + n) * TLD + st * 32 + c * 16 + hh * 8), f, acc[dt]);
+      }
+    }
+  }
+
+  // Depth slots of this wave's positions: the same three products on 32-key
+  // tiles of the packed buffers, read straight from memory (key-major for the
+  // score product; the value and key-transposed operands are gathered).
+  if (wave_active && p.L_d > 0) {
+    const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+    const long long nlo = (long long)tw_min * L_cap + slot_lo;
+    const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
+    const E* kdb = reinterpret_cast<const E*>(p.kd) + (long long)bh * p.NKp * D;
+    const E* vdb = reinterpret_cast<const E*>(p.vd) + (long long)bh * p.NKp * D;
+    for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+      if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const E* krow = kdb + (n0 + key_row) * D + hh * 8;
+      const E* vch = vdb + n0 * D;                 // [D][32] chunk
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mma16(load_frag(krow + kc * 16), qf[kc], s);
+        Frag vf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vf[j] = vch[(kc * 16 + hh * 8 + j) * 32 + key_row];
+        dp = mma16(vf, df[kc], dp);
+      }
+      const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
+      const long long own_hi = own_lo + L_d;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = reg_key(r, hh);
+        const float pr = (key >= own_lo && key < own_hi) ? __builtin_amdgcn_exp2f(s[r] * sl2 - lse2) : 0.f;
+        ds[r] = pr * (dp[r] - dlt);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag f;
+        to_frag(ds + c * 8, f);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          Frag kt;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) kt[j] = kdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
+          acc[dt] = mma16(kt, f, acc[dt]);
+        }
+      }
+    }
+  }
+
+  if (row_ok) {
+    const float sc = p.scale;
+    E* op = reinterpret_cast<E*>(p.dq) + (((long long)b * T + t_row) * p.Hq + hq) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        store4(op + dt * 32 + g4 * 8 + hh * 4, acc[dt][g4 * 4 + 0] * sc, acc[dt][g4 * 4 + 1] * sc,
+               acc[dt][g4 * 4 + 2] * sc, acc[dt][g4 * 4 + 3] * sc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV of the sequence keys: per 32*NW keys of one (b, kvh), every query row
+// at or after the keys' first position.  A lane owns one key: S = Q K^T and
+// dP = dO V^T per 32-row half (queries down), then dV^T += dO^T P and
+// dK^T += Q^T dS.  Q and dO are staged row-major (score operands) and
+// transposed (gradient operands).
+template <typename E, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
+  using Frag = typename Traits<E>::Frag;
+  constexpr int QB = 64;               // query rows per block
+  constexpr int VE = Traits<E>::VE;
+  constexpr int QLD = D + VE;
+  constexpr int TLD = QB + VE;
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int NU = QB * D / (4 * VE);
+  constexpr int UPT = (NU + NT - 1) / NT;
+  static_assert(QB <= NT, "per-row arrays are filled one row per thread");
+
+  __shared__ __attribute__((aligned(16))) E sQ[QB * QLD];
+  __shared__ __attribute__((aligned(16))) E sO[QB * QLD];
+  __shared__ __attribute__((aligned(16))) E sQt[D * TLD];
+  __shared__ __attribute__((aligned(16))) E sOt[D * TLD];
+  __shared__ __attribute__((aligned(16))) float sL[QB];
+  __shared__ __attribute__((aligned(16))) float sDl[QB];
+  __shared__ __attribute__((aligned(16))) int sTq[QB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int ktile = (int)(blockIdx.x / BH);     // earliest keys (most rows) first
+  const int b = bh / p.Hkv;
+  const int kvh = bh % p.Hkv;
+  const int G = p.G;
+  const int T = p.T;
+  const int Hq = p.Hq;
+  const long long TG = (long long)T * G;
+
+  const int kt0 = ktile * (NW * 32);
+  const int wkey0 = kt0 + wave * 32;
+  const int key = wkey0 + n;
+  const bool key_ok = key < T;
+  const bool wave_keys = wkey0 < T;
+
+  const long long kstride = (long long)p.Hkv * D;
+  Frag kf[NKC], vf[NKC];
+  {
+    const long long krow = ((long long)b * T + (key_ok ? key : 0)) * kstride + (long long)kvh * D + hh * 8;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      kf[kc] = key_ok ? load_frag(reinterpret_cast<const E*>(p.k) + krow + kc * 16) : zero_frag<Frag>();
+      vf[kc] = key_ok ? load_frag(reinterpret_cast<const E*>(p.v) + krow + kc * 16) : zero_frag<Frag>();
+    }
+  }
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+
+  const long long rb0 = (long long)kt0 * G / QB * QB;   // first block with a row at position >= kt0
+  const int nqb = (int)((TG - rb0 + QB - 1) / QB);
+  const E* qg = reinterpret_cast<const E*>(p.q);
+  const E* og = reinterpret_cast<const E*>(p.dO);
+
+  u32x4 qreg[UPT][4], oreg[UPT][4];
+  float l_reg = INFINITY, d_reg = 0.f;
+  int t_reg = -1;
+  auto load_block = [&](long long Rb) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      const int rg = u % (QB / 4), dc = u / (QB / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long long Rr = Rb + rg * 4 + r;
+        const bool ok = u < NU && Rr < TG;
+        const long long off = ok ? (((long long)b * T + Rr / G) * Hq + kvh * G + Rr % G) * D + dc * VE : 0;
+        qreg[i][r] = ok ? ld16(qg + off) : u32x4{0, 0, 0, 0};
+        oreg[i][r] = ok ? ld16(og + off) : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < QB) {
+      const long long Rr = Rb + tid;
+      if (Rr < TG) {
+        const int t = (int)(Rr / G);
+        const long long li = ((long long)b * Hq + kvh * G + Rr % G) * T + t;
+        l_reg = p.lse[li] * kLog2e;
+        d_reg = p.delta[li];
+        t_reg = t;
+      } else {
+        l_reg = INFINITY;
+        d_reg = 0.f;
+        t_reg = -1;
+      }
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * NT;
+      if (u >= NU) continue;
+      const int rg = u % (QB / 4), dc = u / (QB / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st16(sQ + (rg * 4 + r) * QLD + dc * VE, qreg[i][r]);
+        st16(sO + (rg * 4 + r) * QLD + dc * VE, oreg[i][r]);
+      }
+      store_t4<E, TLD>(sQt, dc * VE, rg * 4, qreg[i]);
+      store_t4<E, TLD>(sOt, dc * VE, rg * 4, oreg[i]);
+    }
+    if (tid < QB) {
+      sL[tid] = l_reg;
+      sDl[tid] = d_reg;
+      sTq[tid] = t_reg;
+    }
+  };
+
+  const int qperm = key_row_perm(n);   // operand row m holds query row pi(m)
+  const float sl2 = p.scale_log2;
+
+  load_block(rb0);
+  for (int qb = 0; qb < nqb; ++qb) {
+    const long long Rb = rb0 + (long long)qb * QB;
+    __syncthreads();
+    store_block();
+    __syncthreads();
+    if (qb + 1 < nqb) load_block(Rb + QB);
+    if (!wave_keys) continue;
+    const long long Rend = Rb + QB < TG ? Rb + QB : TG;
+    if ((int)((Rend - 1) / G) < wkey0) continue;   // every row of the block precedes this wave's keys
+#pragma unroll
+    for (int sub = 0; sub < QB / 32; ++sub) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const E* qrow = sQ + (sub * 32 + qperm) * QLD + hh * 8;
+      const E* orow = sO + (sub * 32 + qperm) * QLD + hh * 8;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mma16(load_frag(qrow + kc * 16), kf[kc], s);
+        dp = mma16(load_frag(orow + kc * 16), vf[kc], dp);
+      }
+      float pv[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = sub * 32 + reg_key(r, hh);
+        const float pr = sTq[qi] >= key ? __builtin_amdgcn_exp2f(s[r] * sl2 - sL[qi]) : 0.f;
+        pv[r] = pr;
+        ds[r] = pr * (dp[r] - sDl[qi]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        Frag fp, fd;
+        to_frag(pv + c * 8, fp);
+        to_frag(ds + c * 8, fd);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int off = (dt * 32 + n) * TLD + sub * 32 + c * 16 + hh * 8;
+          dv[dt] = mma16(load_frag(sOt + off), fp, dv[dt]);
+          dk[dt] = mma16(load_frag(sQt + off), fd, dk[dt]);
+        }
+      }
+    }
+  }
+
+  if (key_ok) {
+    const float sc = p.scale;
+    const long long orow = (((long long)b * T + key) * p.Hkv + kvh) * D;
+    E* dkp = reinterpret_cast<E*>(p.dk) + orow;
+    E* dvp = reinterpret_cast<E*>(p.dv) + orow;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int e = dt * 32 + g4 * 8 + hh * 4;
+        store4(dkp + e, dk[dt][g4 * 4 + 0] * sc, dk[dt][g4 * 4 + 1] * sc, dk[dt][g4 * 4 + 2] * sc,
+               dk[dt][g4 * 4 + 3] * sc);
+        store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Depth-slot gradients of one (b, t, kv head): the G query heads at t against
+// the L_d slots of t, in float32 on the vector units (the block is
+// G x L_d x d, a few hundred thousand multiply-adds).  Slots in chunks of LC,
+// heads in chunks of GC.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
+  constexpr int GC = 8, LC = 32, LDF = D + 1;   // odd row stride: conflict-free column reads
+  constexpr int EPT = D / 8;                    // outputs per thread and tensor: (slot tid/8, dims tid%8 + 8i)
+  static_assert(GC * LC == 256, "one (head, slot) pair per thread");
+  __shared__ float sq[GC * LDF], sdo[GC * LDF], sk[LC * LDF], sv[LC * LDF];
+  __shared__ float sP[GC * LC], sdS[GC * LC], sLs[GC], sDl[GC];
+
+  const int tid = threadIdx.x;
+  const int Hkv = p.Hkv, T = p.T, Hq = p.Hq, G = p.G, L_d = p.L_d;
+  const int kvh = (int)(blockIdx.x % Hkv);
+  const long long bt = blockIdx.x / Hkv;
+  const int t = (int)(bt % T);
+  const int b = (int)(bt / T);
+  const long long bh = (long long)b * Hkv + kvh;
+  const E* kdb = reinterpret_cast<const E*>(p.kd) + bh * p.NKp * D;
+  const E* vdb = reinterpret_cast<const E*>(p.vd) + bh * p.NKp * D;
+  const E* qg = reinterpret_cast<const E*>(p.q);
+  const E* og = reinterpret_cast<const E*>(p.dO);
+  const float scale = p.scale;
+
+  for (int j0 = 0; j0 < L_d; j0 += LC) {
+    const int nj = L_d - j0 < LC ? L_d - j0 : LC;
+    __syncthreads();
+    // keys: rows of the packed keys, dims fastest
+    for (int i = tid; i < LC * D; i += 256) {
+      const int j = i / D, e = i % D;
+      float kv = 0.f;
+      if (j < nj) kv = (float)kdb[((long long)t * p.L_cap + p.slot_lo + j0 + j) * D + e];
+      sk[j * LDF + e] = kv;
+    }
+    // values: d-major 32-key chunks, keys fastest
+    for (int i = tid; i < LC * D; i += 256) {
+      const int j = i % LC, e = i / LC;
+      float vv = 0.f;
+      if (j < nj) {
+        const long long nk = (long long)t * p.L_cap + p.slot_lo + j0 + j;
+        vv = (float)vdb[(nk / 32) * D * 32 + e * 32 + nk % 32];
+      }
+      sv[j * LDF + e] = vv;
+    }
+    float accK[EPT], accV[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) { accK[i] = 0.f; accV[i] = 0.f; }
+
+    for (int g0 = 0; g0 < G; g0 += GC) {
+      const int ng = G - g0 < GC ? G - g0 : GC;
+      __syncthreads();
+      for (int i = tid; i < GC * D; i += 256) {
+        const int g = i / D, e = i % D;
+        float qv = 0.f, ov = 0.f;
+        if (g < ng) {
+          const long long row = (((long long)b * T + t) * Hq + kvh * G + g0 + g) * D + e;
+          qv = (float)qg[row];
+          ov = (float)og[row];
+        }
+        sq[g * LDF + e] = qv;
+        sdo[g * LDF + e] = ov;
+      }
+      if (tid < GC) {
+        const bool ok = tid < ng;
+        const long long li = ((long long)b * Hq + kvh * G + g0 + tid) * T + t;
+        sLs[tid] = ok ? p.lse[li] : 0.f;
+        sDl[tid] = ok ? p.delta[li] : 0.f;
+      }
+      __syncthreads();
+      {
+        const int g = tid / LC, j = tid % LC;
+        float s = 0.f, dp = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < D; ++e) {
+          s += sq[g * LDF + e] * sk[j * LDF + e];
+          dp += sdo[g * LDF + e] * sv[j * LDF + e];
+        }
+        const bool ok = g < ng && j < nj;
+        const float pr = ok ? __builtin_amdgcn_exp2f((s * scale - sLs[g]) * kLog2e) : 0.f;
+        sP[g * LC + j] = pr;
+        sdS[g * LC + j] = pr * (dp - sDl[g]);
+      }
+      __syncthreads();
+      {
+        const int j = tid / 8, e0 = tid % 8;
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+          const float pp = sP[g * LC + j], dd = sdS[g * LC + j];
+#pragma unroll
+          for (int i = 0; i < EPT; ++i) {
+            accV[i] += pp * sdo[g * LDF + e0 + 8 * i];
+            accK[i] += dd * sq[g * LDF + e0 + 8 * i];
+          }
+        }
+      }
+    }
+    {
+      const int j = tid / 8, e0 = tid % 8;
+      if (j < nj) {
+        const long long orow = ((((long long)b * T + t) * L_d + j0 + j) * Hkv + kvh) * D;
+        E* dkp = reinterpret_cast<E*>(p.dkd) + orow;
+        E* dvp = reinterpret_cast<E*>(p.dvd) + orow;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          dkp[e0 + 8 * i] = (E)(accK[i] * scale);
+          dvp[e0 + 8 * i] = (E)accV[i];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moda

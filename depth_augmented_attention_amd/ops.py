@@ -147,3 +147,68 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                                 _stream(stream))
     check(st, "moda_fwd_window")
     return out, lse
+
+
+def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+             k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
+             out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+             grads: tuple | None = None, delta: torch.Tensor | None = None, stream=None):
+    """Gradients of the MoDA forward.
+
+    q, k_seq, v_seq and the packed depth buffers as for moda_fwd; out and lse
+    are that forward's results; dout [B,T,Hq,d] is the gradient of out.
+    Returns (dq [B,T,Hq,d], dk_seq [B,T,Hkv,d], dv_seq [B,T,Hkv,d],
+    dk_depth [B,T,L_d,Hkv,d], dv_depth [B,T,L_d,Hkv,d]) -- the depth gradients
+    in the logical depth layout (one slot per earlier layer), or None when
+    L_d == 0.  `grads` may supply those five output tensors; `delta` a float32
+    [B,Hq,T] scratch tensor.
+    """
+    if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
+        raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
+    B, T, Hq, d = q.shape
+    Hkv = k_seq.shape[2]
+    if k_seq.shape[:2] != (B, T) or k_seq.shape[3] != d:
+        raise ValueError("k_seq shape does not match q")
+    for t, name in ((k_seq, "k_seq"), (v_seq, "v_seq"), (out, "out"), (dout, "dout")):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have the shape of q")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
+        raise ValueError("lse must be float32 [B,Hq,T]")
+    for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq"), (out, "out"), (lse, "lse"),
+                    (dout, "dout")):
+        _dev(t, name)
+    kd_ptr = vd_ptr = None
+    if L_d > 0:
+        if k_depth is None or v_depth is None:
+            raise ValueError("packed depth buffers are required when L_d > 0")
+        n = depth_packed_elems(B, T, Hkv, d, L_d)
+        for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+            _dev(t, name)
+            if t.numel() != n or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
+        kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
+    shapes = [(B, T, Hq, d), (B, T, Hkv, d), (B, T, Hkv, d), (B, T, L_d, Hkv, d), (B, T, L_d, Hkv, d)]
+    if grads is None:
+        grads = tuple(torch.empty(s, dtype=q.dtype, device=q.device) if (i < 3 or L_d > 0) else None
+                      for i, s in enumerate(shapes))
+    grads = tuple(grads)
+    for i, (g, s) in enumerate(zip(grads, shapes)):
+        if i >= 3 and L_d == 0:
+            continue
+        if g is None or tuple(g.shape) != s or g.dtype != q.dtype:
+            raise ValueError(f"gradient {i} must be {q.dtype} {s}")
+        _dev(g, f"gradient {i}")
+    if delta is None:
+        delta = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _dev(delta, "delta")
+    if delta.dtype != torch.float32 or delta.shape != (B, Hq, T):
+        raise ValueError("delta must be float32 [B,Hq,T]")
+    ptr = [g.data_ptr() if g is not None else None for g in grads]
+    st = load().moda_bwd(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+                         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+                         ptr[3], ptr[4], delta.data_ptr(), B, T, Hq, Hkv, d, L_d, _dtype_code(q),
+                         _stream(stream))
+    check(st, "moda_bwd")
+    return grads

@@ -166,6 +166,40 @@ int moda_append_depth(const void* k_new, const void* v_new,
                       int B, int T, int Hkv, int d, int L_cap, int slot, int dtype,
                       void* stream);
 
+/*
+ * moda_bwd -- gradients of the MoDA forward (moda_fwd with the same L_d).
+ *
+ * The pages present the kernel for training pipelines (gist.science (de)
+ * "Mixture-of-Depths Attention", section 5, Praktische Anwendbarkeit); the
+ * gradients are the derivatives of the forward's definition (mhpn.cn
+ * article, section 1.2 formula, section 2.2 masks).  With P = exp(z - lse),
+ * Delta = rowsum(dout * out), dP = dout . v, dS = P (dP - Delta):
+ *   dq = dS . keys / sqrt(d);  dk = dS^T . q / sqrt(d);  dv = P^T . dout,
+ * summed over every query row (all G heads of the kv head) that sees the key.
+ *
+ *   q, k_seq, v_seq  : in, as for moda_fwd
+ *   k_depth, v_depth : in, packed buffers from moda_pack_depth (NULL iff L_d == 0)
+ *   out, lse         : in, results of moda_fwd on these inputs (lse required)
+ *   dout             : in,  [B, T, Hq, d]  dtype, gradient of out
+ *   dq               : out, [B, T, Hq, d]  dtype
+ *   dk_seq, dv_seq   : out, [B, T, Hkv, d] dtype
+ *   dk_depth, dv_depth : out, [B, T, L_d, Hkv, d] dtype -- the LOGICAL depth
+ *                      layout, slot j being the j-th earlier layer's K/V
+ *                      (NULL iff L_d == 0)
+ *   delta            : scratch, [B, Hq, T] float32, owned by the caller
+ *                      (holds Delta after the call)
+ * Every output element is written (no accumulation into existing contents).
+ * Products use float32 accumulation; P and dS enter them in dtype.  All
+ * outputs must be distinct and must not overlap any input.
+ */
+int moda_bwd(const void* q, const void* k_seq, const void* v_seq,
+             const void* k_depth, const void* v_depth,
+             const void* out, const float* lse, const void* dout,
+             void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+             float* delta,
+             int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+             void* stream);
+
 /* Static, human-readable name of a moda_status value. */
 const char* moda_status_string(int status);
 

@@ -64,6 +64,15 @@ def make_inputs(B, T, Hq, Hkv, d, L_d, dtype="bf16", seed=0, depth=True):
     return q, k_seq, v_seq, k_depth, v_depth
 
 
+def make_dout(B, T, Hq, d, dtype="bf16", seed=0):
+    """Draw the gradient of the output, [B,T,Hq,d] N(0,1) of `dtype`, from its
+    own generator (seed + 500) so that the forward inputs are unchanged."""
+    g = torch.Generator().manual_seed(int(seed) + 500)
+    x = torch.randn(B, T, Hq, d, generator=g, dtype=torch.float32)
+    td = torch_dtype(dtype)
+    return x if td == torch.float32 else x.to(td)
+
+
 def make_workload_inputs(w: dict, depth=True):
     return make_inputs(w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"],
                        dtype=w["dtype"], seed=w["seed"], depth=depth)

@@ -118,3 +118,30 @@ def test_append_validation():
     assert lib.moda_append_depth(None, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 1, 1, None) == _lib.MODA_ERR_NULL
     assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 96, 3, 1, 1, None) == _lib.MODA_ERR_UNSUPPORTED
     assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 1, 4, None) == _lib.MODA_ERR_DTYPE
+
+
+def test_bwd_validation():
+    lib = moda.load()
+    # q k v kd vd out lse dout dq dk dv dkd dvd delta
+    ok = [FAKE] * 14
+    sizes = [1, 4, 2, 1, 128, 3, 1]
+
+    def call(ptrs, sz):
+        return lib.moda_bwd(*ptrs, *sz, None)
+
+    for i in range(14):
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert call(ptrs, sizes) == _lib.MODA_ERR_NULL, f"pointer {i}"
+    # with L_d == 0 the four depth pointers may be NULL (nothing else may)
+    l0 = list(ok)
+    for i in (3, 4, 11, 12):
+        l0[i] = None
+    bad = list(l0)
+    bad[13] = None
+    assert call(bad, [1, 4, 2, 1, 128, 0, 1]) == _lib.MODA_ERR_NULL
+    assert call(ok, [1, 4, 3, 2, 128, 3, 1]) == _lib.MODA_ERR_SHAPE      # Hq % Hkv
+    assert call(ok, [1, 0, 2, 1, 128, 3, 1]) == _lib.MODA_ERR_SHAPE
+    assert call(ok, [1, 4, 2, 1, 128, -1, 1]) == _lib.MODA_ERR_SHAPE
+    assert call(ok, [1, 4, 2, 1, 96, 3, 1]) == _lib.MODA_ERR_UNSUPPORTED
+    assert call(ok, [1, 4, 2, 1, 128, 3, 2]) == _lib.MODA_ERR_DTYPE

@@ -1,0 +1,138 @@
+"""GPU parity of the backward (moda_bwd, through the C ABI) against the
+float64 backward oracle on the same seeded inputs.
+
+The forward that feeds it is the GPU forward (as in training: the backward
+consumes that forward's out and lse).  Each gradient is compared element by
+element; the error is measured relative to max(1, max |reference|) of that
+gradient, since sums over many rows (dk, dv of early keys) grow with T.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import depth_augmented_attention_amd as moda
+from moda_check import np32
+from moda_inputs import make_dout, make_inputs, workload
+from oracle import moda_backward
+
+pytestmark = pytest.mark.gpu
+
+# Bounds on max|gpu - oracle| / max(1, max|oracle|), per gradient.  float32:
+# float32 products end to end.  bf16: P and dS enter the matrix-core products
+# rounded to bf16 (relative 2^-9 each) and every gradient is rounded to bf16
+# on output (relative 2^-9), the same error budget as the forward's 1.5e-2.
+TOL_BWD = {torch.float32: 1e-5, torch.bfloat16: 1.5e-2}
+NAMES = ("dq", "dk_seq", "dv_seq", "dk_depth", "dv_depth")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_fwd_bwd(q, ks, vs, kd, vd, dout):
+    dev = torch.device("cuda:0")
+    L_d = kd.shape[2]
+    qd, kd_, vd_, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    kp = vp = None
+    if L_d > 0:
+        kp, vp = moda.moda_pack_depth(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd(qd, kd_, vd_, kp, vp, L_d)
+    grads = moda.moda_bwd(qd, kd_, vd_, kp, vp, L_d, out, lse, dd)
+    torch.cuda.synchronize()
+    return [None if g is None else g.double().cpu().numpy() for g in grads]
+
+
+def _rel_err(got, ref):
+    if ref.size == 0:
+        return 0.0
+    return float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
+
+
+def _check_all(name, dtype, got, ref):
+    tol = TOL_BWD[dtype]
+    errs = {}
+    for i, nm in enumerate(NAMES):
+        if ref[i].size == 0:
+            continue
+        errs[nm] = _rel_err(got[i], ref[i])
+    _say(f"{name}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{name}: {k} error {v} > {tol}"
+
+
+CASES = [
+    # name, dtype, B, T, Hq, Hkv, d, L_d
+    ("fp32_B1_T128_Hq4_Hkv1_d64_L3", "fp32", 1, 128, 4, 1, 64, 3),
+    ("bf16_T300_G4_d128_L5", "bf16", 1, 300, 8, 2, 128, 5),
+    ("bf16_B2_T97_G3_d128_L4", "bf16", 2, 97, 6, 2, 128, 4),
+    ("bf16_T64_G1_d64_L2", "bf16", 1, 64, 2, 2, 64, 2),
+    ("fp32_T77_G2_d128_L2", "fp32", 1, 77, 4, 2, 128, 2),
+    ("fp32_T150_G3_d64_L7", "fp32", 1, 150, 3, 1, 64, 7),
+    ("bf16_T130_G32_d128_L6", "bf16", 1, 130, 32, 1, 128, 6),
+    ("bf16_T200_G4_d128_L0", "bf16", 1, 200, 4, 1, 128, 0),
+    ("bf16_T1_G2_d128_L3", "bf16", 1, 1, 4, 2, 128, 3),
+    ("bf16_T257_G8_d128_L40", "bf16", 1, 257, 16, 2, 128, 40),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_parity(case):
+    name, dtype, B, T, Hq, Hkv, d, L_d = case
+    _say(f"bwd {name}")
+    seed = 60 + T + Hq
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype=dtype, seed=seed)
+    dout = make_dout(B, T, Hq, d, dtype=dtype, seed=seed)
+    got = run_fwd_bwd(q, ks, vs, kd, vd, dout)
+    ref = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout))
+    if L_d == 0:
+        assert got[3] is None and got[4] is None
+        got = got[:3] + [np.zeros((B, T, 0, Hkv, d))] * 2
+    _check_all(name, q.dtype, got, ref)
+
+
+def test_bwd_workload_T4096_all_elements():
+    w = workload("bf16_B1_T4096_Hq16_Hkv2_d128_L24")
+    _say(f"bwd {w['name']} (all elements)")
+    q, ks, vs, kd, vd = make_inputs(w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"],
+                                    dtype=w["dtype"], seed=w["seed"])
+    dout = make_dout(w["B"], w["T"], w["Hq"], w["d"], dtype=w["dtype"], seed=w["seed"])
+    got = run_fwd_bwd(q, ks, vs, kd, vd, dout)
+    ref = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout))
+    _check_all(w["name"], q.dtype, got, ref)
+
+
+def test_bwd_workload_T65536_sampled():
+    """At the benchmark size: the query and depth-slot gradients of sampled
+    (b, t, kv head) groups against the oracle's per-group form, and the exact
+    sums (sum of dv over all keys = sum of dout; sum of dk = 0) per kv head."""
+    w = workload("bf16_B1_T65536_Hq16_Hkv2_d128_L24")
+    _say(f"bwd {w['name']} (sampled groups + gradient sums)")
+    B, T, Hq, Hkv, d, L_d = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype=w["dtype"], seed=w["seed"])
+    dout = make_dout(B, T, Hq, d, dtype=w["dtype"], seed=w["seed"])
+    dq, dks, dvs, dkd, dvd = run_fwd_bwd(q, ks, vs, kd, vd, dout)
+    G = Hq // Hkv
+    rng = np.random.default_rng(w["seed"] + 11)
+    ts = sorted(set(rng.integers(0, T, 40).tolist()) | {0, 1, 63, 64, T // 2, T - 1})
+    groups = [(0, t, kvh) for t in ts for kvh in range(Hkv)]
+    rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), groups=groups)
+    gq = np.stack([dq[b, t, kvh * G:(kvh + 1) * G] for (b, t, kvh) in groups])
+    gkd = np.stack([dkd[b, t, :, kvh] for (b, t, kvh) in groups])
+    gvd = np.stack([dvd[b, t, :, kvh] for (b, t, kvh) in groups])
+    tol = TOL_BWD[q.dtype]
+    errs = {"dq": _rel_err(gq, rq), "dk_depth": _rel_err(gkd, rkd), "dv_depth": _rel_err(gvd, rvd)}
+    # exact sums, checked relative to the L1 size of the summands
+    do = np32(dout).astype(np.float64)
+    for kvh in range(Hkv):
+        sv = dvs[0, :, kvh].sum(0) + dvd[0, :, :, kvh].sum((0, 1))
+        ref = do[0, :, kvh * G:(kvh + 1) * G].sum((0, 1))
+        l1v = np.abs(dvs[0, :, kvh]).sum(0) + np.abs(dvd[0, :, :, kvh]).sum((0, 1))
+        sk = dks[0, :, kvh].sum(0) + dkd[0, :, :, kvh].sum((0, 1))
+        l1k = np.abs(dks[0, :, kvh]).sum(0) + np.abs(dkd[0, :, :, kvh]).sum((0, 1))
+        errs[f"sum_dv[{kvh}]"] = float((np.abs(sv - ref) / l1v).max())
+        errs[f"sum_dk[{kvh}]"] = float((np.abs(sk) / l1k).max())
+    _say(f"{w['name']}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{k} error {v} > {tol}"
