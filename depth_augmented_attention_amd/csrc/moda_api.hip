@@ -53,7 +53,17 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((moda::moda_bwd_delta_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
   const unsigned BH = (unsigned)(p.B * p.Hkv);
   hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
-  hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+  // the bf16 d=128 kernel addresses one batch's q / dO and lse rows with 32-bit offsets
+  const bool fast = sizeof(E) == 2 && D == 128 && (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL &&
+                    (long long)p.T * p.G * 4 < 0x7fffffffLL;
+  if constexpr (sizeof(E) == 2 && D == 128) {
+    if (fast)
+      hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+  }
   if (p.L_d > 0)
     hipLaunchKernelGGL((moda::moda_bwd_depth_kernel<E, D>), dim3((unsigned)((long long)p.T * BH)), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -195,6 +205,13 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   p.NKp = padded_depth_keys(T, L_d);
   p.scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  {
+    int sh = 0;
+    while ((1LL << sh) < G) ++sh;                                 // ceil(log2 G)
+    const unsigned long long num = 1ULL << (31 + sh);
+    p.g_magic = (uint32_t)((num + (unsigned long long)G - 1) / (unsigned long long)G);
+    p.g_shift = 31 + sh;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

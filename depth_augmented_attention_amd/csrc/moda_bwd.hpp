@@ -31,7 +31,8 @@
 #pragma once
 
 #include "moda_common.hpp"
-#include "moda_fwd.hpp"   // depth_tile_used
+#include "moda_fwd.hpp"        // depth_tile_used
+#include "moda_fwd_bf16.hpp"   // direct-to-LDS loads, LDS transpose reads
 
 namespace moda {
 
@@ -57,9 +58,19 @@ struct BwdParams {
   long long NKp;
   float scale;         // 1 / sqrt(d)
   float scale_log2;    // log2(e) / sqrt(d)
+  uint32_t g_magic;    // x / G == (x * g_magic) >> g_shift for 0 <= x < 2^31
+  int g_shift;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Quotient by the GQA group size through one 32x32->64-bit multiply (the
+// round-up reciprocal of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): exact for 0 <= x < 2^31 with
+// magic = ceil(2^(31+s) / G), s = ceil(log2 G), shift = 31 + s.
+__device__ __forceinline__ int div_g(int x, uint32_t magic, int shift) {
+  return (int)(((uint64_t)(uint32_t)x * magic) >> shift);
+}
 
 // Four rows x VE elements (v[r] = VE consecutive elements of row row0 + r,
 // starting at element e0) written transposed: sT[(e0 + e) * LDT + row0 + r].
@@ -236,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb * BN + st * 32 + reg_key(r, hh);
-        const float pr = key <= t_row ? __builtin_amdgcn_exp2f(s[r] * sl2 - lse2) : 0.f;
+        const float pr = __builtin_amdgcn_exp2f(key <= t_row ? s[r] * sl2 - lse2 : -INFINITY);
         ds[r] = pr * (dp[r] - dlt);
       }
 #pragma unroll
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = reg_key(r, hh);
-        const float pr = (key >= own_lo && key < own_hi) ? __builtin_amdgcn_exp2f(s[r] * sl2 - lse2) : 0.f;
+        const float pr = __builtin_amdgcn_exp2f((key >= own_lo && key < own_hi) ? s[r] * sl2 - lse2 : -INFINITY);
         ds[r] = pr * (dp[r] - dlt);
       }
 #pragma unroll
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
   const int G = p.G;
   const int T = p.T;
   const int Hq = p.Hq;
-  const long long TG = (long long)T * G;
+  const int TG = T * G;   // < 2^31 (checked at the boundary)
 
   const int kt0 = ktile * (NW * 32);
   const int wkey0 = kt0 + wave * 32;
@@ -372,33 +383,34 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < NDT; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  const long long rb0 = (long long)kt0 * G / QB * QB;   // first block with a row at position >= kt0
-  const int nqb = (int)((TG - rb0 + QB - 1) / QB);
+  const int rb0 = kt0 * G / QB * QB;   // first block with a row at position >= kt0
+  const int nqb = (TG - rb0 + QB - 1) / QB;
   const E* qg = reinterpret_cast<const E*>(p.q);
   const E* og = reinterpret_cast<const E*>(p.dO);
 
   u32x4 qreg[UPT][4], oreg[UPT][4];
   float l_reg = INFINITY, d_reg = 0.f;
   int t_reg = -1;
-  auto load_block = [&](long long Rb) {
+  auto load_block = [&](int Rb) {
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * NT;
       const int rg = u % (QB / 4), dc = u / (QB / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const long long Rr = Rb + rg * 4 + r;
+        const int Rr = Rb + rg * 4 + r;
         const bool ok = u < NU && Rr < TG;
-        const long long off = ok ? (((long long)b * T + Rr / G) * Hq + kvh * G + Rr % G) * D + dc * VE : 0;
+        const int t = div_g(Rr, p.g_magic, p.g_shift);
+        const long long off = ok ? (((long long)b * T + t) * Hq + kvh * G + (Rr - t * G)) * D + dc * VE : 0;
         qreg[i][r] = ok ? ld16(qg + off) : u32x4{0, 0, 0, 0};
         oreg[i][r] = ok ? ld16(og + off) : u32x4{0, 0, 0, 0};
       }
     }
     if (tid < QB) {
-      const long long Rr = Rb + tid;
+      const int Rr = Rb + tid;
       if (Rr < TG) {
-        const int t = (int)(Rr / G);
-        const long long li = ((long long)b * Hq + kvh * G + Rr % G) * T + t;
+        const int t = div_g(Rr, p.g_magic, p.g_shift);
+        const long long li = ((long long)b * Hq + kvh * G + (Rr - t * G)) * T + t;
         l_reg = p.lse[li] * kLog2e;
         d_reg = p.delta[li];
         t_reg = t;
@@ -435,14 +447,14 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
 
   load_block(rb0);
   for (int qb = 0; qb < nqb; ++qb) {
-    const long long Rb = rb0 + (long long)qb * QB;
+    const int Rb = rb0 + qb * QB;
     __syncthreads();
     store_block();
     __syncthreads();
     if (qb + 1 < nqb) load_block(Rb + QB);
     if (!wave_keys) continue;
-    const long long Rend = Rb + QB < TG ? Rb + QB : TG;
-    if ((int)((Rend - 1) / G) < wkey0) continue;   // every row of the block precedes this wave's keys
+    const int Rend = Rb + QB < TG ? Rb + QB : TG;
+    if (div_g(Rend - 1, p.g_magic, p.g_shift) < wkey0) continue;   // every row of the block precedes this wave's keys
 #pragma unroll
     for (int sub = 0; sub < QB / 32; ++sub) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -453,13 +465,26 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
         s = mma16(load_frag(qrow + kc * 16), kf[kc], s);
         dp = mma16(load_frag(orow + kc * 16), vf[kc], dp);
       }
+      // the lane's 16 rows are two runs of 8: sub*32 + 16c + 8hh + (0..7)
       float pv[16], ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = sub * 32 + reg_key(r, hh);
-        const float pr = sTq[qi] >= key ? __builtin_amdgcn_exp2f(s[r] * sl2 - sL[qi]) : 0.f;
-        pv[r] = pr;
-        ds[r] = pr * (dp[r] - sDl[qi]);
+      for (int c = 0; c < 2; ++c) {
+        const int q0 = sub * 32 + 16 * c + 8 * hh;
+        const f32x4 la = *reinterpret_cast<const f32x4*>(sL + q0), lb = *reinterpret_cast<const f32x4*>(sL + q0 + 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(sDl + q0), db = *reinterpret_cast<const f32x4*>(sDl + q0 + 4);
+        const u32x4 ta = *reinterpret_cast<const u32x4*>(sTq + q0), tb = *reinterpret_cast<const u32x4*>(sTq + q0 + 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * c + j;
+          const float lr = j < 4 ? la[j] : lb[j - 4];
+          const float dr = j < 4 ? da[j] : db[j - 4];
+          const int tr = (int)(j < 4 ? ta[j] : tb[j - 4]);
+          // masked entries get exponent -inf (select on the argument, no branch)
+          const float x = tr >= key ? s[r] * sl2 - lr : -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(x);
+          pv[r] = pr;
+          ds[r] = pr * (dp[r] - dr);
+        }
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -604,6 +629,277 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, d = 128: dK, dV of the sequence keys laid out for the gfx950 memory
+// path (same computation as moda_bwd_dkdv_kernel).
+//   * Q and dO blocks of 64 rows, with their lse and Delta, go from memory
+//     straight into LDS with the direct global->LDS loads (two stages, one
+//     barrier per block); rows of the GQA fold are gathered by per-lane
+//     offsets, rows past the end read as zeros.
+//   * One copy of each block serves both products: row-major reads for
+//     S = Q K^T and dP = dO V^T, and LDS transpose reads (ds_read_b64_tr_b16)
+//     for the Q^T and dO^T operands of dK^T and dV^T.  The 16-byte chunk index
+//     is XOR-swizzled with 4 (row & 3) + ((row >> 2) & 3), which keeps both
+//     access patterns free of bank conflicts: any 16 consecutive rows get 16
+//     distinct chunks (row reads), and any 4 consecutive rows get 4 distinct
+//     64-byte segments (transpose reads).
+//   * The causal mask needs no division: row R (position R / G) sees key s
+//     iff R >= s * G.
+namespace bwdbf16 {
+
+// physical 16-byte chunk of logical chunk c in row r of a block
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// Sixteen LDS transpose reads: the four Q^T and the four dO^T operand
+// fragments of one 16-row chunk (rows +0 and +4 per fragment half), waited
+// for inside the block.
+template <int OFFQ, int OFFO>
+__device__ __forceinline__ void tr_read_qo(const uint32_t (&a)[8], bf16x8 (&fq)[4], bf16x8 (&fo)[4]) {
+  s16x4 r[16];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]),
+        "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "i"(OFFQ), "i"(OFFO)
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const s16x4 pq[2] = {r[2 * dt], r[2 * dt + 1]};
+    const s16x4 po[2] = {r[8 + 2 * dt], r[8 + 2 * dt + 1]};
+    fq[dt] = *reinterpret_cast<const bf16x8*>(pq);
+    fo[dt] = *reinterpret_cast<const bf16x8*>(po);
+  }
+}
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* ldst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)ldst, 4, voff, 0, 0, 0);
+}
+
+}  // namespace bwdbf16
+
+template <int D>
+__global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "built for head size 128");
+  using namespace bwdbf16;
+  constexpr int NW = 4;
+  constexpr int QB = 64;                       // query rows per block
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE_B = QB * D * 2;           // bytes of a Q (or dO) block
+  constexpr int OFF_O = TILE_B;                // dO block within a stage
+  constexpr int OFF_L = 2 * TILE_B;            // lse[64] within a stage
+  constexpr int OFF_D = 2 * TILE_B + QB * 4;   // Delta[64] within a stage
+  constexpr int STAGE = 2 * TILE_B + 2 * QB * 4;
+  constexpr int LOADS = QB * D / 8 / (NW * 64);   // 16-byte loads per lane per tensor per block
+  constexpr uint32_t OOB = 0x80000000u;         // an offset past every buffer's range: reads zeros
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int ktile = (int)(blockIdx.x / BH);     // earliest keys (most rows) first
+  const int b = bh / p.Hkv;
+  const int kvh = bh % p.Hkv;
+  const int G = p.G;
+  const int T = p.T;
+  const int Hq = p.Hq;
+  const int TG = T * G;
+
+  const int kt0 = ktile * (NW * 32);
+  const int wkey0 = kt0 + wave * 32;
+  const int key = wkey0 + n;
+  const bool key_ok = key < T;
+  const int keyG = key * G;                     // rows R >= keyG see this key
+
+  const long long kstride = (long long)p.Hkv * D;
+  bf16x8 kf[NKC], vf[NKC];
+  {
+    const long long krow = ((long long)b * T + (key_ok ? key : 0)) * kstride + (long long)kvh * D + hh * 8;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      kf[kc] = key_ok ? load_frag(reinterpret_cast<const bf16*>(p.k) + krow + kc * 16) : bf16x8{};
+      vf[kc] = key_ok ? load_frag(reinterpret_cast<const bf16*>(p.v) + krow + kc * 16) : bf16x8{};
+    }
+  }
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+
+  // raw buffers over this (b, kv head)'s rows: q / dO from position 0, head kvh*G;
+  // lse / Delta from head kvh*G of batch b
+  const long long qbase = ((long long)b * T * Hq + (long long)kvh * G) * D;
+  const long long lbase = ((long long)b * Hq + (long long)kvh * G) * T;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const bf16*>(p.q) + qbase), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const bf16*>(p.dO) + qbase), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.lse + lbase), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.delta + lbase), (short)0, 0x7fffffff, kBufferWord3);
+
+  // block of rows [Rb, Rb + 64) -> stage st
+  auto load_block = [&](int Rb, int st) {
+    char* sb = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int sp = i * NW + wave;             // 4-row span of the block
+      const int r = 4 * sp + (lane >> 4);
+      const int R = Rb + r;
+      const int t = div_g(R, p.g_magic, p.g_shift);
+      const int lc = (lane & 15) ^ swz(r);
+      const uint32_t off = R < TG ? (uint32_t)(((t * Hq + (R - t * G)) * D + lc * 8) * 2) : OOB;
+      dma16(rq, off, sb + sp * 1024);
+      dma16(ro, off, sb + OFF_O + sp * 1024);
+    }
+    if (wave == 0) {
+      const int R = Rb + lane;
+      const int t = div_g(R, p.g_magic, p.g_shift);
+      const uint32_t off = R < TG ? (uint32_t)(((R - t * G) * T + t) * 4) : OOB;
+      dma4(rl, off, sb + OFF_L);
+      dma4(rd, off, sb + OFF_D);
+    }
+  };
+
+  // lane-constant LDS byte offsets within a block
+  //  row-major reads: operand row m holds block row pi(m) (+32 for the second half)
+  const int qperm = key_row_perm(n);
+  uint32_t roff[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(qperm * 256 + (((2 * kc + hh) ^ swz(qperm)) * 16));
+  //  transpose reads of a 16-row chunk: 16-lane group q16, lane j16 reads row
+  //  8 (q16 / 2) + j16 / 4 (+4), logical chunk 4 dt + 2 (q16 & 1) + (j16 & 3) / 2,
+  //  half j16 & 1
+  const int q16 = lane >> 4, j16 = lane & 15;
+  const uint32_t sbase = lds_addr(smem);
+  uint32_t tra[8];
+#pragma unroll
+  for (int k4 = 0; k4 < 2; ++k4)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int r = 8 * (q16 >> 1) + (j16 >> 2) + 4 * k4;
+      const int lc = 4 * dt + 2 * (q16 & 1) + ((j16 & 3) >> 1);
+      tra[k4 * 4 + dt] = sbase + (uint32_t)(r * 256 + ((lc ^ swz(r)) * 16) + (j16 & 1) * 8);
+    }
+  // the asm block takes the two rows of a fragment half as separate addresses
+  uint32_t ta[8];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) { ta[2 * dt] = tra[dt]; ta[2 * dt + 1] = tra[4 + dt]; }
+
+  const float sl2 = p.scale_log2;
+  const int rb0 = kt0 * G / QB * QB;            // first block with a row at position >= kt0
+  const int nqb = (TG - rb0 + QB - 1) / QB;
+
+  auto block = [&]<int ST>(int qb) {
+    const int Rb = rb0 + qb * QB;
+    if (qb + 1 < nqb) load_block(Rb + QB, ST ^ 1);
+    if (Rb + QB - 1 >= wkey0 * G) {             // some row of the block sees some key of this wave
+      const char* sb = smem + ST * STAGE;
+      auto half = [&]<int sub>() {
+        bf16x8 qa[NKC], oa[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          qa[kc] = *reinterpret_cast<const bf16x8*>(sb + sub * 32 * 256 + roff[kc]);
+          oa[kc] = *reinterpret_cast<const bf16x8*>(sb + OFF_O + sub * 32 * 256 + roff[kc]);
+        }
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          s = mma16(qa[kc], kf[kc], s);
+          dp = mma16(oa[kc], vf[kc], dp);
+        }
+        bf16x8 pf[2], df[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int q0 = sub * 32 + 16 * c + 8 * hh;   // this lane's 8 rows of the chunk
+          const float* lp = reinterpret_cast<const float*>(sb + OFF_L) + q0;
+          const float* dpp = reinterpret_cast<const float*>(sb + OFF_D) + q0;
+          const f32x4 la = *reinterpret_cast<const f32x4*>(lp), lb = *reinterpret_cast<const f32x4*>(lp + 4);
+          const f32x4 da = *reinterpret_cast<const f32x4*>(dpp), db = *reinterpret_cast<const f32x4*>(dpp + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * c + j;
+            const int R = Rb + q0 + j;
+            const float lr = j < 4 ? la[j] : lb[j - 4];
+            const float dr = j < 4 ? da[j] : db[j - 4];
+            const float x = (R >= keyG && R < TG) ? __builtin_fmaf(s[r], sl2, -lr * kLog2e) : -INFINITY;
+            const float pr = __builtin_amdgcn_exp2f(x);
+            pf[c][j] = (bf16)pr;
+            df[c][j] = (bf16)(pr * (dp[r] - dr));
+          }
+        }
+        bf16x8 fq[NDT], fo[NDT];
+        tr_read_qo<ST * STAGE + sub * 32 * 256, ST * STAGE + OFF_O + sub * 32 * 256>(ta, fq, fo);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = mma16(fo[dt], pf[0], dv[dt]);
+          dk[dt] = mma16(fq[dt], df[0], dk[dt]);
+        }
+        tr_read_qo<ST * STAGE + sub * 32 * 256 + 16 * 256, ST * STAGE + OFF_O + sub * 32 * 256 + 16 * 256>(ta, fq, fo);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = mma16(fo[dt], pf[1], dv[dt]);
+          dk[dt] = mma16(fq[dt], df[1], dk[dt]);
+        }
+      };
+      half.template operator()<0>();
+      half.template operator()<1>();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  load_block(rb0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int qb = 0;
+  for (; qb + 1 < nqb; qb += 2) {
+    block.template operator()<0>(qb);
+    block.template operator()<1>(qb + 1);
+  }
+  if (qb < nqb) block.template operator()<0>(qb);
+
+  if (key_ok) {
+    const float sc = p.scale;
+    const long long orow = (((long long)b * T + key) * p.Hkv + kvh) * D;
+    bf16* dkp = reinterpret_cast<bf16*>(p.dk) + orow;
+    bf16* dvp = reinterpret_cast<bf16*>(p.dv) + orow;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int e = dt * 32 + g4 * 8 + hh * 4;
+        store4(dkp + e, dk[dt][g4 * 4 + 0] * sc, dk[dt][g4 * 4 + 1] * sc, dk[dt][g4 * 4 + 2] * sc,
+               dk[dt][g4 * 4 + 3] * sc);
+        store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
+      }
   }
 }
 
