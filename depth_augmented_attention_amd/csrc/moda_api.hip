@@ -52,7 +52,10 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   const long long rpb = 256 / (D / ve);
   hipLaunchKernelGGL((moda::moda_bwd_delta_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
   const unsigned BH = (unsigned)(p.B * p.Hkv);
-  hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
+  if constexpr (sizeof(E) == 2 && D == 128)
+    hipLaunchKernelGGL((moda::moda_bwd_dq_bf16_kernel<D>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
   // the bf16 d=128 kernel addresses one batch's q / dO and lse rows with 32-bit offsets
   const bool fast = sizeof(E) == 2 && D == 128 && (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL &&
                     (long long)p.T * p.G * 4 < 0x7fffffffLL;

@@ -126,6 +126,74 @@ __global__ __launch_bounds__(256) void moda_bwd_delta_kernel(BwdParams p) {
   }
 }
 
+// Depth slots of one wave's positions [tw_min, tw_max] for dQ: the same
+// three products on 32-key tiles of the packed buffers, read straight from
+// memory (key-major for the score product; the value and key-transposed
+// operands are gathered).  Rows see only their own position's slots.
+template <typename E, int D, typename Frag>
+__device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw_min, int tw_max, int t_row,
+                                              int n, int hh, int key_row, const Frag (&qf)[D / 16],
+                                              const Frag (&df)[D / 16], float lse2, float dlt,
+                                              f32x16 (&acc)[D / 32]) {
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  const float sl2 = p.scale_log2;
+  const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+  const long long nlo = (long long)tw_min * L_cap + slot_lo;
+  const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
+  const E* kdb = reinterpret_cast<const E*>(p.kd) + (long long)bh * p.NKp * D;
+  const E* vdb = reinterpret_cast<const E*>(p.vd) + (long long)bh * p.NKp * D;
+  for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+    if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const E* krow = kdb + (n0 + key_row) * D + hh * 8;
+    const E* vch = vdb + n0 * D;                 // [D][32] chunk
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      s = mma16(load_frag(krow + kc * 16), qf[kc], s);
+      Frag vf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vf[j] = vch[(kc * 16 + hh * 8 + j) * 32 + key_row];
+      dp = mma16(vf, df[kc], dp);
+    }
+    const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
+    const long long own_hi = own_lo + L_d;
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = reg_key(r, hh);
+      const float pr = __builtin_amdgcn_exp2f((key >= own_lo && key < own_hi) ? s[r] * sl2 - lse2 : -INFINITY);
+      ds[r] = pr * (dp[r] - dlt);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      Frag f;
+      to_frag(ds + c * 8, f);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        Frag kt;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kt[j] = kdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
+        acc[dt] = mma16(kt, f, acc[dt]);
+      }
+    }
+  }
+}
+
+// dq = scale * dQ^T accumulator of one lane's row.
+template <typename E, int D>
+__device__ __forceinline__ void dq_store(const BwdParams& p, int b, int t_row, int hq, int hh,
+                                         const f32x16 (&acc)[D / 32]) {
+  const float sc = p.scale;
+  E* op = reinterpret_cast<E*>(p.dq) + (((long long)b * p.T + t_row) * p.Hq + hq) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      store4(op + dt * 32 + g4 * 8 + hh * 4, acc[dt][g4 * 4 + 0] * sc, acc[dt][g4 * 4 + 1] * sc,
+             acc[dt][g4 * 4 + 2] * sc, acc[dt][g4 * 4 + 3] * sc);
+}
+
 // ---------------------------------------------------------------------------
 // dQ: per query tile, S^T = K Q^T and dP^T = V dO^T per 32-key half, then
 // dQ^T += K^T dS^T.  K is staged key-major (score operand) and transposed
@@ -261,62 +329,9 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  // Depth slots of this wave's positions: the same three products on 32-key
-  // tiles of the packed buffers, read straight from memory (key-major for the
-  // score product; the value and key-transposed operands are gathered).
-  if (wave_active && p.L_d > 0) {
-    const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
-    const long long nlo = (long long)tw_min * L_cap + slot_lo;
-    const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
-    const E* kdb = reinterpret_cast<const E*>(p.kd) + (long long)bh * p.NKp * D;
-    const E* vdb = reinterpret_cast<const E*>(p.vd) + (long long)bh * p.NKp * D;
-    for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
-      if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const E* krow = kdb + (n0 + key_row) * D + hh * 8;
-      const E* vch = vdb + n0 * D;                 // [D][32] chunk
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        s = mma16(load_frag(krow + kc * 16), qf[kc], s);
-        Frag vf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vf[j] = vch[(kc * 16 + hh * 8 + j) * 32 + key_row];
-        dp = mma16(vf, df[kc], dp);
-      }
-      const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
-      const long long own_hi = own_lo + L_d;
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = reg_key(r, hh);
-        const float pr = __builtin_amdgcn_exp2f((key >= own_lo && key < own_hi) ? s[r] * sl2 - lse2 : -INFINITY);
-        ds[r] = pr * (dp[r] - dlt);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        Frag f;
-        to_frag(ds + c * 8, f);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          Frag kt;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kt[j] = kdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
-          acc[dt] = mma16(kt, f, acc[dt]);
-        }
-      }
-    }
-  }
-
-  if (row_ok) {
-    const float sc = p.scale;
-    E* op = reinterpret_cast<E*>(p.dq) + (((long long)b * T + t_row) * p.Hq + hq) * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        store4(op + dt * 32 + g4 * 8 + hh * 4, acc[dt][g4 * 4 + 0] * sc, acc[dt][g4 * 4 + 1] * sc,
-               acc[dt][g4 * 4 + 2] * sc, acc[dt][g4 * 4 + 3] * sc);
-  }
+  if (wave_active && p.L_d > 0)
+    dq_depth_fold<E, D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc);
+  if (row_ok) dq_store<E, D>(p, b, t_row, hq, hh, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -692,6 +707,49 @@ __device__ __forceinline__ void tr_read_qo(const uint32_t (&a)[8], bf16x8 (&fq)[
   }
 }
 
+// Eight LDS transpose reads: the four K^T operand fragments of one 16-key
+// chunk, waited for inside the block.
+template <int OFF>
+__device__ __forceinline__ void tr_read8(const uint32_t (&a)[8], bf16x8 (&f)[4]) {
+  s16x4 r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "i"(OFF)
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const s16x4 pr[2] = {r[2 * dt], r[2 * dt + 1]};
+    f[dt] = *reinterpret_cast<const bf16x8*>(pr);
+  }
+}
+
+// lane-constant LDS byte offsets of the transpose reads of a 16-row chunk of a
+// swizzled [rows][128] bf16 block: 16-lane group q16, lane j16 reads row
+// 8 (q16 / 2) + j16 / 4 (+4 for the second half of each fragment), logical
+// chunk 4 dt + 2 (q16 & 1) + (j16 & 3) / 2, half j16 & 1; a[2 dt + k4].
+__device__ __forceinline__ void tr_offsets(int lane, uint32_t base, uint32_t (&a)[8]) {
+  const int q16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int k4 = 0; k4 < 2; ++k4) {
+      const int r = 8 * (q16 >> 1) + (j16 >> 2) + 4 * k4;
+      const int lc = 4 * dt + 2 * (q16 & 1) + ((j16 & 3) >> 1);
+      a[2 * dt + k4] = base + (uint32_t)(r * 256 + ((lc ^ swz(r)) * 16) + (j16 & 1) * 8);
+    }
+}
+
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* ldst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)ldst, 4, voff, 0, 0, 0);
 }
@@ -794,24 +852,8 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   uint32_t roff[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(qperm * 256 + (((2 * kc + hh) ^ swz(qperm)) * 16));
-  //  transpose reads of a 16-row chunk: 16-lane group q16, lane j16 reads row
-  //  8 (q16 / 2) + j16 / 4 (+4), logical chunk 4 dt + 2 (q16 & 1) + (j16 & 3) / 2,
-  //  half j16 & 1
-  const int q16 = lane >> 4, j16 = lane & 15;
-  const uint32_t sbase = lds_addr(smem);
-  uint32_t tra[8];
-#pragma unroll
-  for (int k4 = 0; k4 < 2; ++k4)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int r = 8 * (q16 >> 1) + (j16 >> 2) + 4 * k4;
-      const int lc = 4 * dt + 2 * (q16 & 1) + ((j16 & 3) >> 1);
-      tra[k4 * 4 + dt] = sbase + (uint32_t)(r * 256 + ((lc ^ swz(r)) * 16) + (j16 & 1) * 8);
-    }
-  // the asm block takes the two rows of a fragment half as separate addresses
   uint32_t ta[8];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) { ta[2 * dt] = tra[dt]; ta[2 * dt + 1] = tra[4 + dt]; }
+  tr_offsets(lane, lds_addr(smem), ta);
 
   const float sl2 = p.scale_log2;
   const int rb0 = kt0 * G / QB * QB;            // first block with a row at position >= kt0
@@ -901,6 +943,161 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
         store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, d = 128: dQ laid out like moda_bwd_dkdv_bf16_kernel (same computation
+// as moda_bwd_dq_kernel): K and V blocks of 64 keys go straight into two LDS
+// stages; one swizzled copy of K serves the row-major score operand and, via
+// transpose reads, the K^T operand of dQ^T += K^T dS^T.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moda_bwd_dq_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "built for head size 128");
+  using namespace bwdbf16;
+  constexpr int NW = 4;
+  constexpr int BN = 64;
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE_B = BN * D * 2;
+  constexpr int OFF_V = TILE_B;
+  constexpr int STAGE = 2 * TILE_B;
+  constexpr int LOADS = BN * D / 8 / (NW * 64);
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int tile = p.ntiles - 1 - (int)(blockIdx.x / BH);   // heaviest first
+  const int b = bh / p.Hkv;
+  const int kvh = bh % p.Hkv;
+  const int G = p.G;
+  const int T = p.T;
+  const long long TG = (long long)T * G;
+
+  const long long R0 = (long long)tile * (NW * 32);
+  const long long Rw = R0 + wave * 32;
+  const long long R = Rw + n;
+  const bool row_ok = R < TG;
+  const bool wave_active = Rw < TG;
+  const int t_row = row_ok ? (int)(R / G) : T - 1;
+  const int hq = kvh * G + (row_ok ? (int)(R % G) : 0);
+  const int tw_min = wave_active ? (int)(Rw / G) : T - 1;
+  const int tw_max = wave_active ? (int)((Rw + 31 < TG ? Rw + 31 : TG - 1) / G) : T - 1;
+  const long long Rlast = (R0 + NW * 32 < TG ? R0 + NW * 32 : TG) - 1;
+  const int nblocks = (int)(Rlast / G) / BN + 1;
+
+  const long long qrow = (((long long)b * T + t_row) * p.Hq + hq) * D + hh * 8;
+  bf16x8 qf[NKC], df[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    qf[kc] = row_ok ? load_frag(reinterpret_cast<const bf16*>(p.q) + qrow + kc * 16) : bf16x8{};
+    df[kc] = row_ok ? load_frag(reinterpret_cast<const bf16*>(p.dO) + qrow + kc * 16) : bf16x8{};
+  }
+  const long long lrow = ((long long)b * p.Hq + hq) * T + t_row;
+  const float lse2 = row_ok ? p.lse[lrow] * kLog2e : INFINITY;
+  const float dlt = row_ok ? p.delta[lrow] : 0.f;
+  const float sl2 = p.scale_log2;
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
+
+  const long long kstride = (long long)p.Hkv * D;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long long)b * T * p.Hkv + kvh) * D;
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long long)b * T * p.Hkv + kvh) * D;
+  const int row_bytes = (int)kstride * 2;
+  // span sp of a block is loaded by wave sp % NW: lane l fills row 4 sp + l / 16,
+  // physical chunk l % 16 (logical chunk l % 16 ^ swz(row))
+  uint32_t off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int sp = i * NW + wave;
+    const int r = 4 * sp + (lane >> 4);
+    off[i] = (uint32_t)(r * row_bytes + (((lane & 15) ^ swz(r)) * 16));
+  }
+  auto block_rsrc = [&](const bf16* head, int blk) {
+    const int valid = T - blk * BN;   // >= 1 for every loaded block; rows past it read zeros
+    const int bytes = valid >= BN ? BN * row_bytes : (valid - 1) * row_bytes + D * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(head) + (long long)blk * BN * row_bytes), (short)0, bytes,
+        kBufferWord3);
+  };
+  auto load_block = [&](int blk, int st) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, blk), rv = block_rsrc(vbase, blk);
+    char* sb = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      dma16(rk, off[i], sb + (i * NW + wave) * 1024);
+      dma16(rv, off[i], sb + OFF_V + (i * NW + wave) * 1024);
+    }
+  };
+
+  const int key_row = key_row_perm(n);
+  uint32_t roff[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(key_row * 256 + (((2 * kc + hh) ^ swz(key_row)) * 16));
+  uint32_t ta[8];
+  tr_offsets(lane, lds_addr(smem), ta);
+
+  auto block = [&]<int ST>(int j) {
+    if (j + 1 < nblocks) load_block(j + 1, ST ^ 1);
+    if (wave_active && j * BN <= tw_max) {
+      const char* sb = smem + ST * STAGE;
+      auto half = [&]<int H>() {
+        bf16x8 ka[NKC], va[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          ka[kc] = *reinterpret_cast<const bf16x8*>(sb + H * 32 * 256 + roff[kc]);
+          va[kc] = *reinterpret_cast<const bf16x8*>(sb + OFF_V + H * 32 * 256 + roff[kc]);
+        }
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          s = mma16(ka[kc], qf[kc], s);
+          dp = mma16(va[kc], df[kc], dp);
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * BN + H * 32 + reg_key(r, hh);
+          const float pr = __builtin_amdgcn_exp2f(key <= t_row ? __builtin_fmaf(s[r], sl2, -lse2) : -INFINITY);
+          dsf[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dlt));
+        }
+        bf16x8 kt[NDT];
+        tr_read8<ST * STAGE + H * 32 * 256>(ta, kt);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma16(kt[dt], dsf[0], acc[dt]);
+        tr_read8<ST * STAGE + H * 32 * 256 + 16 * 256>(ta, kt);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma16(kt[dt], dsf[1], acc[dt]);
+      };
+      half.template operator()<0>();
+      half.template operator()<1>();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  load_block(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < nblocks; j += 2) {
+    block.template operator()<0>(j);
+    block.template operator()<1>(j + 1);
+  }
+  if (j < nblocks) block.template operator()<0>(j);
+
+  if (wave_active && p.L_d > 0)
+    dq_depth_fold<bf16, D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc);
+  if (row_ok) dq_store<bf16, D>(p, b, t_row, hq, hh, acc);
 }
 
 }  // namespace moda
