@@ -179,13 +179,13 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
 
 int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
              const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
-             void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* delta, int B, int T,
+             void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B, int T,
              int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
-  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || !delta)
+  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || !work)
     return MODA_ERR_NULL;
   if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
@@ -199,7 +199,7 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
 
   moda::BwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
-  p.o = out; p.dO = dout; p.lse = lse; p.delta = delta;
+  p.o = out; p.dO = dout; p.lse = lse; p.work = work; p.BHT = (long long)B * Hq * T;
   p.dq = dq; p.dk = dk_seq; p.dv = dv_seq; p.dkd = dk_depth; p.dvd = dv_depth;
   p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
   p.L_d = L_d; p.L_cap = L_d > 0 ? L_d : 1; p.slot_lo = 0;

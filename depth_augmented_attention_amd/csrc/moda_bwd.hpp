@@ -10,7 +10,11 @@
 //   dS_ij = P_ij (dP_ij - Delta_i)  dQ_i = scale sum_j dS_ij k_j
 //   dK_j = scale sum_i dS_ij q_i
 // Four kernels, all on the caller's stream in this order:
-//   moda_bwd_delta_kernel  Delta [B,Hq,T] from out and dO.
+//   moda_bwd_delta_kernel  -Delta and -lse*sqrt(d), two [B,Hq,T] planes of a
+//                          float32 work buffer; they seed the dP and S
+//                          accumulators of the kernels below, so that the
+//                          products come out as dP - Delta and as scores
+//                          already shifted by lse.
 //   moda_bwd_dq_kernel     one workgroup per query tile (rows fold GQA as in
 //                          the forward: row R is position R / G, head
 //                          kvh*G + R % G); sweeps the causal key blocks like
@@ -30,6 +34,8 @@
 // probabilities and dS enter them in the input precision.
 #pragma once
 
+#include <utility>
+
 #include "moda_common.hpp"
 #include "moda_fwd.hpp"        // depth_tile_used
 #include "moda_fwd_bf16.hpp"   // direct-to-LDS loads, LDS transpose reads
@@ -45,7 +51,8 @@ struct BwdParams {
   const void* o;       // forward output [B,T,Hq,D]
   const void* dO;      // gradient of the output [B,T,Hq,D]
   const float* lse;    // forward lse [B,Hq,T] (natural log)
-  float* delta;        // [B,Hq,T], written by the first kernel
+  float* work;         // [2][B,Hq,T]: -Delta, then -lse*sqrt(d); written by the first kernel
+  long long BHT;       // B * Hq * T (plane size of work)
   void* dq;            // [B,T,Hq,D]
   void* dk;            // [B,T,Hkv,D]
   void* dv;
@@ -98,7 +105,8 @@ __device__ __forceinline__ void store_t4(E* sT, int e0, int row0, const u32x4 (&
 }
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * out), one 16-byte chunk per thread.
+// Delta = rowsum(dO * out), one 16-byte chunk per thread; stores -Delta and
+// -lse / scale (= -lse * sqrt(d)).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void moda_bwd_delta_kernel(BwdParams p) {
   constexpr int VE = Traits<E>::VE;
@@ -122,7 +130,9 @@ __global__ __launch_bounds__(256) void moda_bwd_delta_kernel(BwdParams p) {
     const long long bt = row / p.Hq;
     const int t = (int)(bt % p.T);
     const int b = (int)(bt / p.T);
-    p.delta[((long long)b * p.Hq + h) * p.T + t] = s;
+    const long long i = ((long long)b * p.Hq + h) * p.T + t;
+    p.work[i] = -s;
+    p.work[p.BHT + i] = -p.lse[i] / p.scale;
   }
 }
 
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
   }
   const long long lrow = ((long long)b * p.Hq + hq) * T + t_row;
   const float lse2 = row_ok ? p.lse[lrow] * kLog2e : INFINITY;   // P = 0 on rows past the end
-  const float dlt = row_ok ? p.delta[lrow] : 0.f;
+  const float dlt = row_ok ? -p.work[lrow] : 0.f;
   const float sl2 = p.scale_log2;
 
   f32x16 acc[NDT];
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dkdv_kernel(BwdParams p) {
         const int t = div_g(Rr, p.g_magic, p.g_shift);
         const long long li = ((long long)b * Hq + kvh * G + (Rr - t * G)) * T + t;
         l_reg = p.lse[li] * kLog2e;
-        d_reg = p.delta[li];
+        d_reg = -p.work[li];
         t_reg = t;
       } else {
         l_reg = INFINITY;
@@ -601,7 +611,7 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
         const bool ok = tid < ng;
         const long long li = ((long long)b * Hq + kvh * G + g0 + tid) * T + t;
         sLs[tid] = ok ? p.lse[li] : 0.f;
-        sDl[tid] = ok ? p.delta[li] : 0.f;
+        sDl[tid] = ok ? -p.work[li] : 0.f;
       }
       __syncthreads();
       {
@@ -762,12 +772,13 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   using namespace bwdbf16;
   constexpr int NW = 4;
   constexpr int QB = 64;                       // query rows per block
+  constexpr int NSUB = QB / 32;                // 32-row sub-blocks per block
   constexpr int NKC = D / 16;
   constexpr int NDT = D / 32;
   constexpr int TILE_B = QB * D * 2;           // bytes of a Q (or dO) block
   constexpr int OFF_O = TILE_B;                // dO block within a stage
-  constexpr int OFF_L = 2 * TILE_B;            // lse[64] within a stage
-  constexpr int OFF_D = 2 * TILE_B + QB * 4;   // Delta[64] within a stage
+  constexpr int OFF_L = 2 * TILE_B;            // lse[QB] within a stage
+  constexpr int OFF_D = 2 * TILE_B + QB * 4;   // Delta[QB] within a stage
   constexpr int STAGE = 2 * TILE_B + 2 * QB * 4;
   constexpr int LOADS = QB * D / 8 / (NW * 64);   // 16-byte loads per lane per tensor per block
   constexpr uint32_t OOB = 0x80000000u;         // an offset past every buffer's range: reads zeros
@@ -818,10 +829,10 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
       (void*)(reinterpret_cast<const bf16*>(p.q) + qbase), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const bf16*>(p.dO) + qbase), (short)0, 0x7fffffff, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.lse + lbase), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.delta + lbase), (short)0, 0x7fffffff, kBufferWord3);
+      (void*)(p.work + lbase), (short)0, 0x7fffffff, kBufferWord3);          // -Delta
+  const __amdgpu_buffer_rsrc_t rl2 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.work + p.BHT + lbase), (short)0, 0x7fffffff, kBufferWord3);  // -lse * sqrt(d)
 
   // block of rows [Rb, Rb + 64) -> stage st
   auto load_block = [&](int Rb, int st) {
@@ -837,12 +848,12 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
       dma16(rq, off, sb + sp * 1024);
       dma16(ro, off, sb + OFF_O + sp * 1024);
     }
-    if (wave == 0) {
-      const int R = Rb + lane;
+    if (wave < QB / 64) {
+      const int R = Rb + wave * 64 + lane;
       const int t = div_g(R, p.g_magic, p.g_shift);
       const uint32_t off = R < TG ? (uint32_t)(((R - t * G) * T + t) * 4) : OOB;
-      dma4(rl, off, sb + OFF_L);
-      dma4(rd, off, sb + OFF_D);
+      dma4(rl2, off, sb + OFF_L + wave * 256);
+      dma4(rd, off, sb + OFF_D + wave * 256);
     }
   };
 
@@ -852,67 +863,105 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   uint32_t roff[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(qperm * 256 + (((2 * kc + hh) ^ swz(qperm)) * 16));
-  uint32_t ta[8];
-  tr_offsets(lane, lds_addr(smem), ta);
+  uint32_t ta0[8], ta1[8];   // transpose-read addresses in stage 0 and stage 1
+  tr_offsets(lane, lds_addr(smem), ta0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ta1[i] = ta0[i] + STAGE;
 
   const float sl2 = p.scale_log2;
   const int rb0 = kt0 * G / QB * QB;            // first block with a row at position >= kt0
   const int nqb = (TG - rb0 + QB - 1) / QB;
 
+  // S and dP of 32-row sub-block `sub` of the block in stage ST, their
+  // accumulators seeded with -lse*sqrt(d) and -Delta of each row: s holds
+  // S - lse*sqrt(d) and dp holds dP - Delta.  The lane's 16 rows are two runs
+  // of 8: sub*32 + 16c + 8hh + (0..7).
+  auto products = [&]<int ST, int sub>(f32x16& s, f32x16& dp) {
+    const char* sb = smem + ST * STAGE;
+    bf16x8 qa[NKC], oa[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      qa[kc] = *reinterpret_cast<const bf16x8*>(sb + sub * 32 * 256 + roff[kc]);
+      oa[kc] = *reinterpret_cast<const bf16x8*>(sb + OFF_O + sub * 32 * 256 + roff[kc]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int q0 = sub * 32 + 16 * c + 8 * hh;
+      const f32x4* lp = reinterpret_cast<const f32x4*>(sb + OFF_L + q0 * 4);
+      const f32x4* dpp = reinterpret_cast<const f32x4*>(sb + OFF_D + q0 * 4);
+      const f32x4 la = lp[0], lb = lp[1], da = dpp[0], db = dpp[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[8 * c + j] = la[j];
+        s[8 * c + 4 + j] = lb[j];
+        dp[8 * c + j] = da[j];
+        dp[8 * c + 4 + j] = db[j];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      s = mma16(qa[kc], kf[kc], s);
+      dp = mma16(oa[kc], vf[kc], dp);
+    }
+  };
+  // P = 2^((S - lse sqrt(d)) log2(e) / sqrt(d)) and dS = P (dP - Delta) as
+  // bf16 operand fragments; MASKED applies the causal condition
+  // R >= key * G (rows past the end need no mask: their q and dO are zero, so
+  // they add nothing)
+  auto softmax = [&]<int sub, bool MASKED>(int Rb, const f32x16& s, const f32x16& dp, bf16x8 (&pf)[2],
+                                           bf16x8 (&df)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * c + j;
+        float x = s[r] * sl2;
+        if constexpr (MASKED) x = Rb + sub * 32 + 16 * c + 8 * hh + j >= keyG ? x : -INFINITY;
+        const float pr = __builtin_amdgcn_exp2f(x);
+        pf[c][j] = (bf16)pr;
+        df[c][j] = (bf16)(pr * dp[r]);
+      }
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over one sub-block
+  auto update = [&]<int ST, int sub>(const bf16x8 (&pf)[2], const bf16x8 (&df)[2]) {
+    bf16x8 fq[NDT], fo[NDT];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (c == 0)
+        tr_read_qo<sub * 32 * 256, OFF_O + sub * 32 * 256>(ST ? ta1 : ta0, fq, fo);
+      else
+        tr_read_qo<sub * 32 * 256 + 4096, OFF_O + sub * 32 * 256 + 4096>(ST ? ta1 : ta0, fq, fo);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        dv[dt] = mma16(fo[dt], pf[c], dv[dt]);
+        dk[dt] = mma16(fq[dt], df[c], dk[dt]);
+      }
+    }
+  };
+  // all sub-blocks, the products of the next issued before the softmax of
+  // the current so that matrix and vector work overlap within the wave
+  auto compute = [&]<int ST, bool MASKED>(int Rb) {
+    f32x16 s[2], dp[2];
+    products.template operator()<ST, 0>(s[0], dp[0]);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ([&] {
+        if constexpr (I + 1 < NSUB) products.template operator()<ST, I + 1>(s[(I + 1) & 1], dp[(I + 1) & 1]);
+        bf16x8 pf[2], df[2];
+        softmax.template operator()<I, MASKED>(Rb, s[I & 1], dp[I & 1], pf, df);
+        update.template operator()<ST, I>(pf, df);
+      }(), ...);
+    }(std::make_integer_sequence<int, NSUB>{});
+  };
+
   auto block = [&]<int ST>(int qb) {
     const int Rb = rb0 + qb * QB;
     if (qb + 1 < nqb) load_block(Rb + QB, ST ^ 1);
     if (Rb + QB - 1 >= wkey0 * G) {             // some row of the block sees some key of this wave
-      const char* sb = smem + ST * STAGE;
-      auto half = [&]<int sub>() {
-        bf16x8 qa[NKC], oa[NKC];
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          qa[kc] = *reinterpret_cast<const bf16x8*>(sb + sub * 32 * 256 + roff[kc]);
-          oa[kc] = *reinterpret_cast<const bf16x8*>(sb + OFF_O + sub * 32 * 256 + roff[kc]);
-        }
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          s = mma16(qa[kc], kf[kc], s);
-          dp = mma16(oa[kc], vf[kc], dp);
-        }
-        bf16x8 pf[2], df[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int q0 = sub * 32 + 16 * c + 8 * hh;   // this lane's 8 rows of the chunk
-          const float* lp = reinterpret_cast<const float*>(sb + OFF_L) + q0;
-          const float* dpp = reinterpret_cast<const float*>(sb + OFF_D) + q0;
-          const f32x4 la = *reinterpret_cast<const f32x4*>(lp), lb = *reinterpret_cast<const f32x4*>(lp + 4);
-          const f32x4 da = *reinterpret_cast<const f32x4*>(dpp), db = *reinterpret_cast<const f32x4*>(dpp + 4);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = 8 * c + j;
-            const int R = Rb + q0 + j;
-            const float lr = j < 4 ? la[j] : lb[j - 4];
-            const float dr = j < 4 ? da[j] : db[j - 4];
-            const float x = (R >= keyG && R < TG) ? __builtin_fmaf(s[r], sl2, -lr * kLog2e) : -INFINITY;
-            const float pr = __builtin_amdgcn_exp2f(x);
-            pf[c][j] = (bf16)pr;
-            df[c][j] = (bf16)(pr * (dp[r] - dr));
-          }
-        }
-        bf16x8 fq[NDT], fo[NDT];
-        tr_read_qo<ST * STAGE + sub * 32 * 256, ST * STAGE + OFF_O + sub * 32 * 256>(ta, fq, fo);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = mma16(fo[dt], pf[0], dv[dt]);
-          dk[dt] = mma16(fq[dt], df[0], dk[dt]);
-        }
-        tr_read_qo<ST * STAGE + sub * 32 * 256 + 16 * 256, ST * STAGE + OFF_O + sub * 32 * 256 + 16 * 256>(ta, fq, fo);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = mma16(fo[dt], pf[1], dv[dt]);
-          dk[dt] = mma16(fq[dt], df[1], dk[dt]);
-        }
-      };
-      half.template operator()<0>();
-      half.template operator()<1>();
+      if (Rb >= (wkey0 + 31) * G)               // every row sees every key of this wave
+        compute.template operator()<ST, false>(Rb);
+      else
+        compute.template operator()<ST, true>(Rb);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -1002,7 +1051,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   }
   const long long lrow = ((long long)b * p.Hq + hq) * T + t_row;
   const float lse2 = row_ok ? p.lse[lrow] * kLog2e : INFINITY;
-  const float dlt = row_ok ? p.delta[lrow] : 0.f;
+  const float dlt = row_ok ? -p.work[lrow] : 0.f;
   const float sl2 = p.scale_log2;
 
   f32x16 acc[NDT];

@@ -152,7 +152,7 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
 def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
              k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
              out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
-             grads: tuple | None = None, delta: torch.Tensor | None = None, stream=None):
+             grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
     """Gradients of the MoDA forward.
 
     q, k_seq, v_seq and the packed depth buffers as for moda_fwd; out and lse
@@ -160,8 +160,8 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     Returns (dq [B,T,Hq,d], dk_seq [B,T,Hkv,d], dv_seq [B,T,Hkv,d],
     dk_depth [B,T,L_d,Hkv,d], dv_depth [B,T,L_d,Hkv,d]) -- the depth gradients
     in the logical depth layout (one slot per earlier layer), or None when
-    L_d == 0.  `grads` may supply those five output tensors; `delta` a float32
-    [B,Hq,T] scratch tensor.
+    L_d == 0.  `grads` may supply those five output tensors; `work` a float32
+    [2,B,Hq,T] scratch tensor.
     """
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
@@ -200,15 +200,15 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
         if g is None or tuple(g.shape) != s or g.dtype != q.dtype:
             raise ValueError(f"gradient {i} must be {q.dtype} {s}")
         _dev(g, f"gradient {i}")
-    if delta is None:
-        delta = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
-    _dev(delta, "delta")
-    if delta.dtype != torch.float32 or delta.shape != (B, Hq, T):
-        raise ValueError("delta must be float32 [B,Hq,T]")
+    if work is None:
+        work = torch.empty(2, B, Hq, T, dtype=torch.float32, device=q.device)
+    _dev(work, "work")
+    if work.dtype != torch.float32 or work.shape != (2, B, Hq, T):
+        raise ValueError("work must be float32 [2,B,Hq,T]")
     ptr = [g.data_ptr() if g is not None else None for g in grads]
     st = load().moda_bwd(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
                          out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
-                         ptr[3], ptr[4], delta.data_ptr(), B, T, Hq, Hkv, d, L_d, _dtype_code(q),
+                         ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_d, _dtype_code(q),
                          _stream(stream))
     check(st, "moda_bwd")
     return grads

@@ -186,8 +186,9 @@ int moda_append_depth(const void* k_new, const void* v_new,
  *   dk_depth, dv_depth : out, [B, T, L_d, Hkv, d] dtype -- the LOGICAL depth
  *                      layout, slot j being the j-th earlier layer's K/V
  *                      (NULL iff L_d == 0)
- *   delta            : scratch, [B, Hq, T] float32, owned by the caller
- *                      (holds Delta after the call)
+ *   work             : scratch, 2 * B * Hq * T float32, owned by the caller
+ *                      (after the call: -Delta, then -lse * sqrt(d), each
+ *                      [B, Hq, T])
  * Every output element is written (no accumulation into existing contents).
  * Products use float32 accumulation; P and dS enter them in dtype.  All
  * outputs must be distinct and must not overlap any input.
@@ -196,7 +197,7 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq,
              const void* k_depth, const void* v_depth,
              const void* out, const float* lse, const void* dout,
              void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
-             float* delta,
+             float* work,
              int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
              void* stream);
 

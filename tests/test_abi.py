@@ -122,7 +122,7 @@ def test_append_validation():
 
 def test_bwd_validation():
     lib = moda.load()
-    # q k v kd vd out lse dout dq dk dv dkd dvd delta
+    # q k v kd vd out lse dout dq dk dv dkd dvd work
     ok = [FAKE] * 14
     sizes = [1, 4, 2, 1, 128, 3, 1]
 
