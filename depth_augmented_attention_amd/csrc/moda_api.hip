@@ -100,8 +100,10 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
   if (L_d == 0) return MODA_OK;
   if (!k_depth || !v_depth || !k_packed || !v_packed) return MODA_ERR_NULL;
+  if ((long long)T * L_d > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;
   moda::PackParams p{k_depth, v_depth, k_packed, v_packed, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
-  const long long grid = (long long)B * Hkv * (p.NKp / 32);
+  const int ve = dtype == MODA_BF16 ? 8 : 4;
+  const long long grid = ((long long)B * Hkv * p.NKp * (d / ve) + 255) / 256;
   if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

@@ -47,7 +47,7 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* kd;      // packed depth keys   [B][Hkv][NKp][D]
-  const void* vd;      // packed depth values [B][Hkv][NKp/32][D][32]
+  const void* vd;      // packed depth values [B][Hkv][NKp][D]
   const void* o;       // forward output [B,T,Hq,D]
   const void* dO;      // gradient of the output [B,T,Hq,D]
   const float* lse;    // forward lse [B,Hq,T] (natural log)
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256) void moda_bwd_delta_kernel(BwdParams p) {
 
 // Depth slots of one wave's positions [tw_min, tw_max] for dQ: the same
 // three products on 32-key tiles of the packed buffers, read straight from
-// memory (key-major for the score product; the value and key-transposed
-// operands are gathered).  Rows see only their own position's slots.
+// memory (key-major rows for the score and dP products; the key-transposed
+// operand of dQ is gathered).  Rows see only their own position's slots.
 template <typename E, int D, typename Frag>
 __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw_min, int tw_max, int t_row,
                                               int n, int hh, int key_row, const Frag (&qf)[D / 16],
@@ -157,14 +157,11 @@ __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw
     if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
     f32x16 s = f32x16{}, dp = f32x16{};
     const E* krow = kdb + (n0 + key_row) * D + hh * 8;
-    const E* vch = vdb + n0 * D;                 // [D][32] chunk
+    const E* vrow = vdb + (n0 + key_row) * D + hh * 8;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       s = mma16(load_frag(krow + kc * 16), qf[kc], s);
-      Frag vf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vf[j] = vch[(kc * 16 + hh * 8 + j) * 32 + key_row];
-      dp = mma16(vf, df[kc], dp);
+      dp = mma16(load_frag(vrow + kc * 16), df[kc], dp);
     }
     const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
     const long long own_hi = own_lo + L_d;
@@ -579,14 +576,11 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
       if (j < nj) kv = (float)kdb[((long long)t * p.L_cap + p.slot_lo + j0 + j) * D + e];
       sk[j * LDF + e] = kv;
     }
-    // values: d-major 32-key chunks, keys fastest
+    // values: rows of the packed values, dims fastest
     for (int i = tid; i < LC * D; i += 256) {
-      const int j = i % LC, e = i / LC;
+      const int j = i / D, e = i % D;
       float vv = 0.f;
-      if (j < nj) {
-        const long long nk = (long long)t * p.L_cap + p.slot_lo + j0 + j;
-        vv = (float)vdb[(nk / 32) * D * 32 + e * 32 + nk % 32];
-      }
+      if (j < nj) vv = (float)vdb[((long long)t * p.L_cap + p.slot_lo + j0 + j) * D + e];
       sv[j * LDF + e] = vv;
     }
     float accK[EPT], accV[EPT];

@@ -34,7 +34,7 @@ struct FwdParams {
   const void* k;
   const void* v;
   const void* kd;   // packed depth keys   [B][Hkv][NKp][D]
-  const void* vd;   // packed depth values [B][Hkv][NKp/32][D][32]
+  const void* vd;   // packed depth values [B][Hkv][NKp][D]
   void* out;
   float* lse;
   int B, T, Hq, Hkv, G;
@@ -274,14 +274,19 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
         sv[r] = (key >= own_lo && key < own_hi) ? acc[r] * sl2 : -INFINITY;
       }
       online_update<E>(sv, m_run, l_run, o);
-      const E* vchunk = vdb + n0 * D;   // [D][32] block of this 32-key chunk
+      // V^T operand: 8 consecutive keys of head dimension dt*32 + n, gathered
+      // from the key-major packed rows
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         Frag pf;
         to_frag(sv + c * 8, pf);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = mma16(load_frag(vchunk + (dt * 32 + n) * 32 + c * 16 + hh * 8), pf, o[dt]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          Frag vt;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vt[j] = vdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
+          o[dt] = mma16(vt, pf, o[dt]);
+        }
       }
     }
   }

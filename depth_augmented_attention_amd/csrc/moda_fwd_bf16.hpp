@@ -330,6 +330,12 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
     const bf16* kdb = reinterpret_cast<const bf16*>(p.kd) + (long long)bh * p.NKp * D;
     const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
+    // the stages are free after the last barrier of the sweep: wave w uses
+    // 32 rows (8 KB) at row 32 w of the first stage pair for its depth values
+    bf16* vwave = smem + wave * 32 * D;
+    uint32_t vaw[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vaw[dt] = va[dt] + (uint32_t)(wave * 32 * D * 2);
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
@@ -360,12 +366,26 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       }
       bf16x8 pf[2];
       l_run += exps(sv, -m_run, pf);
-      const bf16* vchunk = vdb + n0 * D;
+      // V^T operand through this wave's LDS region: the 32 key-major value
+      // rows with the V-stage swizzle, then the same transpose reads as the
+      // sequence blocks
+      {
+        u32x4 vr[8];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int i = 0; i < 8; ++i) vr[i] = ld16(vdb + (n0 + 4 * i + (lane >> 4)) * D + (lane & 15) * 8);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = mma16(load_frag(vchunk + (dt * 32 + n) * 32 + c * 16 + hh * 8), pf[c], o[dt]);
+        for (int i = 0; i < 8; ++i) {
+          const int r = 4 * i + (lane >> 4);
+          st16(vwave + r * D + (((lane & 15) ^ (4 * (r & 3))) * 8), vr[i]);
+        }
+      }
+      bf16x8 vf[4];
+      tr_read_chunk<0>(vaw, vf);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[0], o[dt]);
+      tr_read_chunk<16 * D * 2>(vaw, vf);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[1], o[dt]);
     }
   }
 

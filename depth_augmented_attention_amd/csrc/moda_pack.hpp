@@ -8,12 +8,11 @@
 // Attention", Technische Zusammenfassung section 2, Flash-Compatible Layout and
 // Chunk-Aware Layout; mhpn.cn article section 2.1, chunked contiguous
 // storage).  This kernel writes, per (b, kv head), key n = t * L_d + j:
-//   k_packed [B][Hkv][NKp][D]          rows of d elements
-//   v_packed [B][Hkv][NKp/32][D][32]   32-key chunks stored d-major
-// with zero rows for n >= T * L_d.  One workgroup handles one 32-key chunk:
-// it reads 32 rows coalesced, copies the keys through, and transposes the
-// values through LDS so that both writes are contiguous 8 KB (bf16, d = 128)
-// blocks.
+//   k_packed [B][Hkv][NKp][D]   rows of d elements
+//   v_packed [B][Hkv][NKp][D]   the same for the values
+// with zero rows for n >= T * L_d (NKp = T * L_d rounded up to 32).  One
+// thread per 16-byte chunk of a packed row; reads and writes are contiguous
+// 16-byte accesses.
 #pragma once
 
 #include "moda_common.hpp"
@@ -32,43 +31,24 @@ struct PackParams {
 template <typename E, int D>
 __global__ __launch_bounds__(256) void moda_pack_depth_kernel(PackParams p) {
   constexpr int VE = Traits<E>::VE;
-  constexpr int LD = D + VE;
-  __shared__ __attribute__((aligned(16))) E tile[32 * LD];
-
-  const long long nchunks = p.NKp / 32;
-  const long long chunk = blockIdx.x % nchunks;
-  const int bh = (int)(blockIdx.x / nchunks);
-  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
-  const long long n0 = chunk * 32;
-  const long long nvalid = (long long)p.T * p.L_d;
-
-  const E* kd = reinterpret_cast<const E*>(p.kd);
-  const E* vd = reinterpret_cast<const E*>(p.vd);
-  E* kp = reinterpret_cast<E*>(p.kp) + ((long long)bh * p.NKp + n0) * D;
-  E* vp = reinterpret_cast<E*>(p.vp) + ((long long)bh * p.NKp + n0) * D;
-
-  for (int c = threadIdx.x; c < 32 * D / VE; c += 256) {
-    const int row = c / (D / VE), col = c % (D / VE);
-    const long long key = n0 + row;
-    u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-    if (key < nvalid) {
-      const long long t = key / p.L_d, j = key % p.L_d;
-      const long long src = (((long long)b * p.T + t) * p.L_d + j) * p.Hkv * D + (long long)kvh * D + col * VE;
-      kv = ld16(kd + src);
-      vv = ld16(vd + src);
-    }
-    st16(kp + row * D + col * VE, kv);
-    st16(tile + row * LD + col * VE, vv);
+  constexpr int CPR = D / VE;                   // 16-byte chunks per row
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rows = (long long)p.B * p.Hkv * p.NKp;
+  if (idx >= rows * CPR) return;
+  const long long row = idx / CPR;              // (bh, n) in packed order
+  const int c = (int)(idx % CPR);
+  const long long bh = row / p.NKp;
+  const int n = (int)(row % p.NKp);             // T * L_d < 2^31 (checked at the boundary)
+  const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
+  u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+  if (n < p.T * p.L_d) {
+    const int t = n / p.L_d, j = n - t * p.L_d;
+    const long long src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D + c * VE;
+    kv = ld16(reinterpret_cast<const E*>(p.kd) + src);
+    vv = ld16(reinterpret_cast<const E*>(p.vd) + src);
   }
-  __syncthreads();
-  // values: [D][32] -- each thread writes VE consecutive keys of one dim
-  for (int c = threadIdx.x; c < D * 32 / VE; c += 256) {
-    const int dim = c / (32 / VE), k0 = (c % (32 / VE)) * VE;
-    E vals[VE];
-#pragma unroll
-    for (int e = 0; e < VE; ++e) vals[e] = tile[(k0 + e) * LD + dim];
-    st16(vp + dim * 32 + k0, *reinterpret_cast<const u32x4*>(vals));
-  }
+  st16(reinterpret_cast<E*>(p.kp) + row * D + c * VE, kv);
+  st16(reinterpret_cast<E*>(p.vp) + row * D + c * VE, vv);
 }
 
 }  // namespace moda
@@ -81,9 +61,9 @@ namespace moda {
 // Zusammenfassung section 2, Write-Step).  Same packed layout as
 // moda_pack_depth_kernel with L_cap slots per position:
 //   k_packed[b][kvh][t * L_cap + slot][:]   = k_new[b][t][kvh][:]
-//   v_packed[b][kvh][n / 32][e][n % 32]      = v_new[b][t][kvh][e],  n = t * L_cap + slot
-// One thread per 16-byte chunk of one (b, t, kvh) row: the key chunk is one
-// 16-byte store, the value chunk VE strided element stores.
+//   v_packed[b][kvh][t * L_cap + slot][:]   = v_new[b][t][kvh][:]
+// One thread per 16-byte chunk of one (b, t, kvh) row: one 16-byte load and
+// one 16-byte store per tensor.
 struct AppendParams {
   const void* k_new;
   const void* v_new;
@@ -111,12 +91,9 @@ __global__ __launch_bounds__(256) void moda_append_depth_kernel(AppendParams p) 
   const E* ks = reinterpret_cast<const E*>(p.k_new) + row * D + c * VE;
   const E* vs = reinterpret_cast<const E*>(p.v_new) + row * D + c * VE;
   E* kd = reinterpret_cast<E*>(p.kp) + (bh * p.NKp + n) * D + c * VE;
+  E* vd = reinterpret_cast<E*>(p.vp) + (bh * p.NKp + n) * D + c * VE;
   st16(kd, ld16(ks));
-  E vals[VE];
-  *reinterpret_cast<u32x4*>(vals) = ld16(vs);
-  E* vd = reinterpret_cast<E*>(p.vp) + bh * p.NKp * D + (n / 32) * D * 32 + (n % 32);
-#pragma unroll
-  for (int e = 0; e < VE; ++e) vd[(c * VE + e) * 32] = vals[e];
+  st16(vd, ld16(vs));
 }
 
 }  // namespace moda

@@ -77,12 +77,10 @@ long long moda_depth_packed_elems(int B, int T, int Hkv, int d, int L_d);
  * for each (b, kv head):
  *
  *   k_depth, v_depth : in,  logical [B, T, L_d, Hkv, d], dtype
- *   k_packed         : out, [B, Hkv, NKp, d]            key n = t * L_d + j
- *   v_packed         : out, [B, Hkv, NKp / 32, d, 32]   the same keys in
- *                      chunks of 32, each chunk stored d-major (value
- *                      transposed), as the fused kernel's matrix-core operand
- *                      wants it.
- *   Keys n >= T * L_d (padding up to NKp) are written as zeros.
+ *   k_packed         : out, [B, Hkv, NKp, d]   key n = t * L_d + j
+ *   v_packed         : out, [B, Hkv, NKp, d]   value n = t * L_d + j
+ *   Keys n >= T * L_d (padding up to NKp) are written as zeros.  T * L_d
+ *   must stay below 2^31 - 32.
  *   Each packed buffer holds moda_depth_packed_elems(...) elements.
  *
  * With L_d == 0 nothing is enqueued and all four pointers may be NULL.

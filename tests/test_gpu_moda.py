@@ -90,11 +90,10 @@ def _pack_reference(kd: np.ndarray, vd: np.ndarray):
     n = T * L_d
     NKp = (n + 31) // 32 * 32
     kp = np.zeros((B, Hkv, NKp, d), dtype=kd.dtype)
-    vflat = np.zeros((B, Hkv, NKp, d), dtype=vd.dtype)
+    vp = np.zeros((B, Hkv, NKp, d), dtype=vd.dtype)
     kp[:, :, :n] = np.transpose(kd, (0, 3, 1, 2, 4)).reshape(B, Hkv, n, d)
-    vflat[:, :, :n] = np.transpose(vd, (0, 3, 1, 2, 4)).reshape(B, Hkv, n, d)
-    vp = vflat.reshape(B, Hkv, NKp // 32, 32, d).transpose(0, 1, 2, 4, 3)
-    return kp.reshape(-1), np.ascontiguousarray(vp).reshape(-1)
+    vp[:, :, :n] = np.transpose(vd, (0, 3, 1, 2, 4)).reshape(B, Hkv, n, d)
+    return kp.reshape(-1), vp.reshape(-1)
 
 
 @pytest.mark.parametrize("case", [("bf16", 2, 37, 3, 128, 5), ("fp32", 1, 64, 2, 64, 3), ("bf16", 1, 40, 1, 64, 24)])
