@@ -949,8 +949,11 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   };
 
   auto block = [&]<int ST>(int qb) {
-    const int Rb = rb0 + qb * QB;
-    if (qb + 1 < nqb) load_block(Rb + QB, ST ^ 1);
+    // blocks are swept from the last rows back to the keys' first position, so
+    // that the workgroups of all key tiles read the same rows at about the
+    // same time (they share them in L2) and the masked blocks come last
+    const int Rb = rb0 + (nqb - 1 - qb) * QB;
+    if (qb + 1 < nqb) load_block(Rb - QB, ST ^ 1);
     if (Rb + QB - 1 >= wkey0 * G) {             // some row of the block sees some key of this wave
       if (Rb >= (wkey0 + 31) * G)               // every row sees every key of this wave
         compute.template operator()<ST, false>(Rb);
@@ -961,7 +964,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
     __syncthreads();
   };
 
-  load_block(rb0, 0);
+  load_block(rb0 + (nqb - 1) * QB, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int qb = 0;
