@@ -280,6 +280,33 @@ def main():
         res["window_fwd_tflops"] = (4.0 * B * Hq * d * (T * (T + 1) / 2 + T * (L_d - lo))) / (win_ms * 1e-3) / 1e12
         if "fwd_ms_L0" in res:
             res["window_overhead_vs_L0"] = win_ms / res["fwd_ms_L0"] - 1.0
+        # 8-bit depth KV: quantising repack and the forward over int8 codes
+        log("timing 8-bit depth KV (pack_q8, fwd_q8)")
+        packed = moda.moda_pack_depth_q8(kd, vd)
+        moda.moda_fwd_q8(q, ks, vs, packed, L_d, out=out, lse=lse)
+        torch.cuda.synchronize()
+        eq = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        for i in range(3):
+            eq[i].record()
+            moda.moda_pack_depth_q8(kd, vd)
+        eq[3].record()
+        for i in range(3):
+            moda.moda_fwd_q8(q, ks, vs, packed, L_d, out=out, lse=lse)
+            eq[4 + i].record()
+        torch.cuda.synchronize()
+        q8_pack_ms = eq[0].elapsed_time(eq[3]) / 3
+        q8_fwd_ms = eq[3].elapsed_time(eq[6]) / 3
+        depth_elems = kd.numel()
+        q8_bytes = 2 * depth_elems + 2 * 4 * (depth_elems // d)       # codes + row scales, K and V
+        res["q8_depth_bytes"] = q8_bytes
+        res["depth_bytes"] = 2 * depth_elems * kd.element_size()
+        res["q8_pack_ms"] = q8_pack_ms
+        res["q8_pack_gbps"] = (res["depth_bytes"] + q8_bytes) / (q8_pack_ms * 1e-3) / 1e9
+        res["q8_fwd_ms"] = q8_fwd_ms
+        res["q8_fwd_tflops"] = F / (q8_fwd_ms * 1e-3) / 1e12
+        if "fwd_ms_L0" in res:
+            res["q8_overhead_vs_L0"] = q8_fwd_ms / res["fwd_ms_L0"] - 1.0
+        del packed
 
     if not args.no_bwd:
         # backward of the same forward: dq, dk/dv of sequence and depth keys

@@ -17,6 +17,8 @@ from .ops import (  # noqa: F401
     moda_append_depth,
     moda_bwd,
     moda_fwd,
+    moda_fwd_q8,
     moda_fwd_window,
     moda_pack_depth,
+    moda_pack_depth_q8,
 )

@@ -19,7 +19,8 @@ MODA_ERR_HIP = 5
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
-           "moda_append_depth", "moda_bwd", "moda_status_string")
+           "moda_append_depth", "moda_bwd", "moda_pack_depth_q8", "moda_fwd_q8",
+           "moda_status_string")
 
 
 class ModaError(RuntimeError):
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.moda_append_depth.restype = c_int
     lib.moda_bwd.argtypes = [c_vp] * 14 + [c_int] * 7 + [c_vp]
     lib.moda_bwd.restype = c_int
+    lib.moda_pack_depth_q8.argtypes = [c_vp] * 6 + [c_int] * 6 + [c_vp]
+    lib.moda_pack_depth_q8.restype = c_int
+    lib.moda_fwd_q8.argtypes = [c_vp] * 9 + [c_int] * 7 + [c_vp]
+    lib.moda_fwd_q8.restype = c_int
     lib.moda_status_string.argtypes = [c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     _lib = lib

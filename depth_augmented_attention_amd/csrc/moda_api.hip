@@ -114,9 +114,10 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
-int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
-                    const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
-                    int L_cap, int slot_lo, int slot_hi, int dtype, void* stream) {
+static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, const float* k_scale, const float* v_scale, int q8, void* out,
+                    float* lse, int B, int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi,
+                    int dtype, void* stream) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
@@ -125,6 +126,7 @@ int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const v
   if (!q || !k_seq || !v_seq || !out) return MODA_ERR_NULL;
   const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth)) return MODA_ERR_NULL;
+  if (L_d > 0 && q8 && (!k_scale || !v_scale)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
   const int tile_rows = rows_per_tile(dtype, d);
@@ -134,6 +136,7 @@ int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const v
 
   moda::FwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
+  p.ksc = k_scale; p.vsc = v_scale; p.q8 = q8;
   p.out = out; p.lse = lse;
   p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
   p.L_d = L_d; p.L_cap = L_cap > 0 ? L_cap : 1; p.slot_lo = slot_lo;
@@ -148,6 +151,46 @@ int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const v
   else
     e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, s) : launch_fwd<float, 64>(p, (unsigned)grid, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
+                    int L_cap, int slot_lo, int slot_hi, int dtype, void* stream) {
+  return fwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, B, T, Hq, Hkv, d,
+                  L_cap, slot_lo, slot_hi, dtype, stream);
+}
+
+int moda_fwd_q8(const void* q, const void* k_seq, const void* v_seq, const int8_t* k_q,
+                const int8_t* v_q, const float* k_scale, const float* v_scale, void* out, float* lse,
+                int B, int T, int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return fwd_impl(q, k_seq, v_seq, k_q, v_q, k_scale, v_scale, 1, out, lse, B, T, Hq, Hkv, d, L_d, 0,
+                  L_d, dtype, stream);
+}
+
+int moda_pack_depth_q8(const void* k_depth, const void* v_depth, int8_t* k_q, int8_t* v_q,
+                       float* k_scale, float* v_scale, int B, int T, int Hkv, int d, int L_d, int dtype,
+                       void* stream) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (L_d == 0) return MODA_OK;
+  if (!k_depth || !v_depth || !k_q || !v_q || !k_scale || !v_scale) return MODA_ERR_NULL;
+  if ((long long)T * L_d > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;
+  moda::PackQ8Params p{k_depth, v_depth, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
+  const long long rows = (long long)B * Hkv * p.NKp;
+  const long long rpb = 256 / (d / 8);
+  const long long grid = (rows + rpb - 1) / rpb;
+  if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == MODA_BF16) {
+    if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  }
+  return hipGetLastError() == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
 int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,

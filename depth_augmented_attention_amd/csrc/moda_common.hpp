@@ -75,6 +75,39 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// Eight int8 codes (8 bytes at p) times a float32 scale, as a fragment of the
+// element type (8-bit depth KV: one scale per packed key or value row).
+__device__ __forceinline__ void dequant8(const int8_t* p, float scale, float (&v)[8]) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int code = (int)(int8_t)(w[j >> 2] >> (8 * (j & 3)));
+    v[j] = scale * (float)code;
+  }
+}
+__device__ __forceinline__ bf16x8 dequant_frag_bf16(const int8_t* p, float scale) {
+  float v[8];
+  dequant8(p, scale, v);
+  bf16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (bf16)v[j];
+  return f;
+}
+__device__ __forceinline__ f32x8 dequant_frag_f32(const int8_t* p, float scale) {
+  float v[8];
+  dequant8(p, scale, v);
+  return f32x8{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+}
+template <typename E> struct Dequant;
+template <> struct Dequant<bf16> {
+  static __device__ __forceinline__ bf16x8 frag(const int8_t* p, float s) { return dequant_frag_bf16(p, s); }
+  static __device__ __forceinline__ bf16 one(int8_t c, float s) { return (bf16)(s * (float)c); }
+};
+template <> struct Dequant<float> {
+  static __device__ __forceinline__ f32x8 frag(const int8_t* p, float s) { return dequant_frag_f32(p, s); }
+  static __device__ __forceinline__ float one(int8_t c, float s) { return s * (float)c; }
+};
+
 // Row order of the 32-key operand tiles.  A 32x32 accumulator gives lane half
 // h the rows {8q + 4h + i : q = 0..3, i = 0..3}; loading key pi(m) into operand
 // row m (pi swaps bits 2 and 3 of m) makes the 16 values a lane holds be the

@@ -33,8 +33,11 @@ struct FwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* kd;   // packed depth keys   [B][Hkv][NKp][D]
+  const void* kd;   // packed depth keys   [B][Hkv][NKp][D] (dtype, or int8 codes when q8)
   const void* vd;   // packed depth values [B][Hkv][NKp][D]
+  const float* ksc; // q8: float32 scale per packed key row   [B][Hkv][NKp]
+  const float* vsc; // q8: float32 scale per packed value row [B][Hkv][NKp]
+  int q8;           // depth KV stored as int8 codes + row scales
   void* out;
   float* lse;
   int B, T, Hq, Hkv, G;
@@ -262,9 +265,17 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
-      const E* krow = kdb + (n0 + key_row) * D + hh * 8;
+      if (p.q8) {
+        const long long kr = (long long)bh * p.NKp + n0 + key_row;
+        const int8_t* krow = reinterpret_cast<const int8_t*>(p.kd) + kr * D + hh * 8;
+        const float ks = p.ksc[kr];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+        for (int kc = 0; kc < NKC; ++kc) acc = mma16(Dequant<E>::frag(krow + kc * 16, ks), qf[kc], acc);
+      } else {
+        const E* krow = kdb + (n0 + key_row) * D + hh * 8;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+      }
       float sv[16];
       const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;   // this row's slots,
       const long long own_hi = own_lo + L_d;                              // relative to n0
@@ -284,7 +295,15 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
         for (int dt = 0; dt < NDT; ++dt) {
           Frag vt;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) vt[j] = vdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
+          for (int j = 0; j < 8; ++j) {
+            const long long key = n0 + c * 16 + hh * 8 + j;
+            if (p.q8) {
+              const long long vr = (long long)bh * p.NKp + key;
+              vt[j] = Dequant<E>::one(reinterpret_cast<const int8_t*>(p.vd)[vr * D + dt * 32 + n], p.vsc[vr]);
+            } else {
+              vt[j] = vdb[key * D + dt * 32 + n];
+            }
+          }
           o[dt] = mma16(vt, pf, o[dt]);
         }
       }

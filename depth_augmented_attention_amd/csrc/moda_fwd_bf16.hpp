@@ -339,9 +339,17 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
-      const bf16* krow = kdb + (n0 + key_row) * D + hh * 8;
+      if (p.q8) {
+        const long long kr = (long long)bh * p.NKp + n0 + key_row;
+        const int8_t* krow = reinterpret_cast<const int8_t*>(p.kd) + kr * D + hh * 8;
+        const float ks = p.ksc[kr];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+        for (int kc = 0; kc < NKC; ++kc) acc = mma16(dequant_frag_bf16(krow + kc * 16, ks), qf[kc], acc);
+      } else {
+        const bf16* krow = kdb + (n0 + key_row) * D + hh * 8;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+      }
       // same arithmetic as a sequence half-block: masked raw scores, one FMA
       // into exp2; the max is exact here (these tiles are few) and the sum is
       // taken over the bf16-rounded probabilities that enter P.V
@@ -372,7 +380,16 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       {
         u32x4 vr[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vr[i] = ld16(vdb + (n0 + 4 * i + (lane >> 4)) * D + (lane & 15) * 8);
+        for (int i = 0; i < 8; ++i) {
+          const long long row = n0 + 4 * i + (lane >> 4);
+          if (p.q8) {
+            const long long r = (long long)bh * p.NKp + row;
+            const bf16x8 f = dequant_frag_bf16(reinterpret_cast<const int8_t*>(p.vd) + r * D + (lane & 15) * 8, p.vsc[r]);
+            vr[i] = *reinterpret_cast<const u32x4*>(&f);
+          } else {
+            vr[i] = ld16(vdb + row * D + (lane & 15) * 8);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 4 * i + (lane >> 4);

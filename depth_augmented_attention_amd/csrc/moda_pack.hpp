@@ -97,3 +97,90 @@ __global__ __launch_bounds__(256) void moda_append_depth_kernel(AppendParams p) 
 }
 
 }  // namespace moda
+
+namespace moda {
+
+// 8-bit depth KV (a memory tip of the mhpn.cn article, section 4.2): the same
+// packed rows as moda_pack_depth_kernel, each stored as d int8 codes plus one
+// float32 scale, scale = max|x| / 127 and code = rint(x / scale) clamped to
+// +-127 (0 for an all-zero row), every step in float32.  LPR lanes per packed
+// row, 8 elements each; the row maximum is reduced across those lanes.
+struct PackQ8Params {
+  const void* kd;
+  const void* vd;
+  int8_t* kq;
+  int8_t* vq;
+  float* ks;
+  float* vs;
+  int B, T, Hkv, L_d;
+  long long NKp;
+};
+
+template <typename E>
+__device__ __forceinline__ void load8(const E* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 f = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (float)f[j];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+}
+
+__device__ __forceinline__ u32x2 quantize8(const float (&x)[8], float scale) {
+  u32x2 w = {0u, 0u};
+  if (scale > 0.f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float c = rintf(x[j] / scale);
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      w[j >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (j & 3));
+    }
+  }
+  return w;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p) {
+  constexpr int LPR = D / 8;                    // lanes per packed row
+  constexpr int RPB = 256 / LPR;                // rows per workgroup
+  const long long rows = (long long)p.B * p.Hkv * p.NKp;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int l = threadIdx.x % LPR;
+  float xk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (row < rows) {
+    const long long bh = row / p.NKp;
+    const int n = (int)(row % p.NKp);
+    if (n < p.T * p.L_d) {
+      const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
+      const int t = n / p.L_d, j = n - t * p.L_d;
+      const long long src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D + l * 8;
+      load8(reinterpret_cast<const E*>(p.kd) + src, xk);
+      load8(reinterpret_cast<const E*>(p.vd) + src, xv);
+    }
+  }
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { mk = fmaxf(mk, fabsf(xk[j])); mv = fmaxf(mv, fabsf(xv[j])); }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, off));
+    mv = fmaxf(mv, __shfl_xor(mv, off));
+  }
+  const float sk = mk / 127.f, sv = mv / 127.f;
+  if (row < rows) {
+    *reinterpret_cast<u32x2*>(p.kq + row * D + l * 8) = quantize8(xk, sk);
+    *reinterpret_cast<u32x2*>(p.vq + row * D + l * 8) = quantize8(xv, sv);
+    if (l == 0) {
+      p.ks[row] = sk;
+      p.vs[row] = sv;
+    }
+  }
+}
+
+}  // namespace moda

@@ -212,3 +212,66 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                          _stream(stream))
     check(st, "moda_bwd")
     return grads
+
+
+def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None):
+    """8-bit packed depth KV: returns (k_q, v_q int8 flat buffers of
+    depth_packed_elems(...) codes, k_scale, v_scale float32 [elems / d])."""
+    if k_depth.dim() != 5 or v_depth.shape != k_depth.shape or v_depth.dtype != k_depth.dtype:
+        raise ValueError("k_depth / v_depth must both be [B,T,L_d,Hkv,d] of one dtype")
+    B, T, L_d, Hkv, d = k_depth.shape
+    n = depth_packed_elems(B, T, Hkv, d, L_d)
+    dev = k_depth.device
+    kq = torch.empty(n, dtype=torch.int8, device=dev)
+    vq = torch.empty(n, dtype=torch.int8, device=dev)
+    ks = torch.empty(n // d, dtype=torch.float32, device=dev)
+    vs = torch.empty(n // d, dtype=torch.float32, device=dev)
+    if L_d == 0:
+        return kq, vq, ks, vs
+    for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+        _dev(t, name)
+    st = load().moda_pack_depth_q8(k_depth.data_ptr(), v_depth.data_ptr(), kq.data_ptr(), vq.data_ptr(),
+                                   ks.data_ptr(), vs.data_ptr(), B, T, Hkv, d, L_d,
+                                   _dtype_code(k_depth), _stream(stream))
+    check(st, "moda_pack_depth_q8")
+    return kq, vq, ks, vs
+
+
+def moda_fwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8, L_d: int,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                with_lse: bool = True, stream=None):
+    """MoDA forward over 8-bit depth KV (the four buffers of moda_pack_depth_q8)."""
+    if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
+        raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
+    B, T, Hq, d = q.shape
+    Hkv = k_seq.shape[2]
+    if k_seq.shape[:2] != (B, T) or k_seq.shape[3] != d:
+        raise ValueError("k_seq shape does not match q")
+    if k_seq.dtype != q.dtype or v_seq.dtype != q.dtype:
+        raise ValueError("q, k_seq, v_seq must share one dtype")
+    for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq")):
+        _dev(t, name)
+    ptrs = [None] * 4
+    if L_d > 0:
+        kq, vq, ks, vs = packed_q8
+        n = depth_packed_elems(B, T, Hkv, d, L_d)
+        for t, name, dt, cnt in ((kq, "k_q", torch.int8, n), (vq, "v_q", torch.int8, n),
+                                 (ks, "k_scale", torch.float32, n // d), (vs, "v_scale", torch.float32, n // d)):
+            _dev(t, name)
+            if t.dtype != dt or t.numel() != cnt:
+                raise ValueError(f"{name} must hold {cnt} elements of {dt}")
+        ptrs = [kq.data_ptr(), vq.data_ptr(), ks.data_ptr(), vs.data_ptr()]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    if with_lse and lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse")
+        if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
+            raise ValueError("lse must be float32 [B,Hq,T]")
+    st = load().moda_fwd_q8(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs, out.data_ptr(),
+                            lse.data_ptr() if lse is not None else None, B, T, Hq, Hkv, d, L_d,
+                            _dtype_code(q), _stream(stream))
+    check(st, "moda_fwd_q8")
+    return out, lse

@@ -39,6 +39,8 @@
 #ifndef MODA_H
 #define MODA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -163,6 +165,44 @@ int moda_append_depth(const void* k_new, const void* v_new,
                       void* k_packed, void* v_packed,
                       int B, int T, int Hkv, int d, int L_cap, int slot, int dtype,
                       void* stream);
+
+/*
+ * moda_pack_depth_q8 -- moda_pack_depth with 8-bit depth KV.
+ *
+ * The mhpn.cn article (section 4.2, memory optimisation) suggests 8-bit
+ * quantisation for the depth KV of deep models; the format is not given.
+ * Here: symmetric int8 per packed row (one key or value vector of d
+ * elements) with one float32 scale, decided in float32:
+ *   scale = max|x| / 127,  code = rint(x / scale) clamped to [-127, 127]
+ *   (ties to even; an all-zero row has scale 0 and codes 0),
+ *   dequantised value = scale * code.
+ *
+ *   k_depth, v_depth : in,  logical [B, T, L_d, Hkv, d], dtype
+ *   k_q, v_q         : out, int8 [B, Hkv, NKp, d], the packed order of
+ *                      moda_pack_depth (moda_depth_packed_elems(...) bytes each)
+ *   k_scale, v_scale : out, float32 [B, Hkv, NKp] (elems / d floats each)
+ *   Padding rows (n >= T * L_d) get scale 0 and codes 0.
+ * With L_d == 0 nothing is enqueued and the pointers may be NULL.
+ */
+int moda_pack_depth_q8(const void* k_depth, const void* v_depth,
+                       int8_t* k_q, int8_t* v_q, float* k_scale, float* v_scale,
+                       int B, int T, int Hkv, int d, int L_d, int dtype,
+                       void* stream);
+
+/*
+ * moda_fwd_q8 -- moda_fwd reading 8-bit depth KV from moda_pack_depth_q8.
+ * The depth keys and values are dequantised (scale * code, rounded to dtype)
+ * in registers before the matrix products; the result is the MoDA forward of
+ * the dequantised depth KV.  Arguments as for moda_fwd, with the packed
+ * buffers replaced by the int8 codes and float32 row scales (NULL iff
+ * L_d == 0).
+ */
+int moda_fwd_q8(const void* q, const void* k_seq, const void* v_seq,
+                const int8_t* k_q, const int8_t* v_q,
+                const float* k_scale, const float* v_scale,
+                void* out, float* lse,
+                int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+                void* stream);
 
 /*
  * moda_bwd -- gradients of the MoDA forward (moda_fwd with the same L_d).

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "moda.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moda_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moda_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_matches_binding():
@@ -145,3 +145,17 @@ def test_bwd_validation():
     assert call(ok, [1, 4, 2, 1, 128, -1, 1]) == _lib.MODA_ERR_SHAPE
     assert call(ok, [1, 4, 2, 1, 96, 3, 1]) == _lib.MODA_ERR_UNSUPPORTED
     assert call(ok, [1, 4, 2, 1, 128, 3, 2]) == _lib.MODA_ERR_DTYPE
+
+
+def test_q8_validation():
+    lib = moda.load()
+    # pack: L_d == 0 is a no-op with NULL pointers; a NULL scale is rejected
+    assert lib.moda_pack_depth_q8(None, None, None, None, None, None, 1, 4, 1, 128, 0, 1, None) == _lib.MODA_OK
+    assert lib.moda_pack_depth_q8(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 128, 3, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_pack_depth_q8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 100, 3, 1, None) == _lib.MODA_ERR_UNSUPPORTED
+    assert lib.moda_pack_depth_q8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 9, None) == _lib.MODA_ERR_DTYPE
+    # forward: scales are required when slots are read
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.moda_fwd_q8(*args, None, FAKE, FAKE, None, 1, 4, 2, 1, 128, 3, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_fwd_q8(*args, FAKE, FAKE, FAKE, None, 1, 4, 3, 2, 128, 3, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_fwd_q8(*args, FAKE, FAKE, FAKE, None, 1, 4, 2, 1, 128, -1, 1, None) == _lib.MODA_ERR_SHAPE

@@ -1,0 +1,140 @@
+"""GPU parity of 8-bit depth KV: moda_pack_depth_q8 codes and scales bit for
+bit against the oracle's quantisation, and moda_fwd_q8 against the forward
+oracle on the dequantised depth KV."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import depth_augmented_attention_amd as moda
+from moda_check import TOL, np32
+from moda_inputs import make_inputs, sample_rows, workload
+from oracle import moda_forward
+from oracle.moda_quant import dequantize_rows, quantize_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _packed_rows(x):
+    """Logical [B,T,L,Hkv,d] -> packed row order [B,Hkv,T*L,d] (no padding)."""
+    B, T, L, Hkv, d = x.shape
+    return np.transpose(x, (0, 3, 1, 2, 4)).reshape(B, Hkv, T * L, d)
+
+
+def _ref_q8(kd, vd):
+    """Oracle codes / scales in the packed order, with zero padding rows."""
+    B, T, L, Hkv, d = kd.shape
+    NKp = (T * L + 31) // 32 * 32
+    out = []
+    for x in (kd, vd):
+        codes, scales = quantize_rows(_packed_rows(np32(x)))
+        c = np.zeros((B, Hkv, NKp, d), np.int8)
+        s = np.zeros((B, Hkv, NKp), np.float32)
+        c[:, :, :T * L] = codes
+        s[:, :, :T * L] = scales
+        out += [c.reshape(-1), s.reshape(-1)]
+    return out
+
+
+def _with_zero_rows(kd, vd):
+    kd = kd.clone()
+    vd = vd.clone()
+    kd[0, 0, 0] = 0          # all-zero key rows (scale 0)
+    vd[0, -1, -1] = 0
+    return kd, vd
+
+
+@pytest.mark.parametrize("case", [("bf16", 2, 37, 3, 128, 5), ("fp32", 1, 64, 2, 64, 3),
+                                  ("bf16", 1, 40, 1, 64, 24), ("fp32", 1, 9, 2, 128, 2)])
+def test_pack_q8_bitwise(case):
+    dtype, B, T, Hkv, d, L = case
+    _say(f"pack q8 {case}")
+    _, _, _, kd, vd = make_inputs(B, T, Hkv, Hkv, d, L, dtype=dtype, seed=9)
+    kd, vd = _with_zero_rows(kd, vd)
+    kq, vq, ks, vs = moda.moda_pack_depth_q8(kd.cuda(), vd.cuda())
+    torch.cuda.synchronize()
+    rkq, rks, rvq, rvs = _ref_q8(kd, vd)
+    assert np.array_equal(kq.cpu().numpy(), rkq)
+    assert np.array_equal(vq.cpu().numpy(), rvq)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+
+
+def _deq_logical(kd):
+    """Oracle dequantised depth tensor in the logical layout (float64)."""
+    codes, scales = quantize_rows(np32(kd))
+    return dequantize_rows(codes, scales)
+
+
+def _run(q, ks, vs, kd, vd):
+    dev = torch.device("cuda:0")
+    L = kd.shape[2]
+    packed = moda.moda_pack_depth_q8(kd.to(dev), vd.to(dev)) if L > 0 else None
+    out, lse = moda.moda_fwd_q8(q.to(dev), ks.to(dev), vs.to(dev), packed, L)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(name, dtype, out, lse, ref_out, ref_lse):
+    tol = TOL[dtype]
+    eo = float(np.abs(out.double().cpu().numpy() - ref_out).max())
+    el = float(np.abs(lse.double().cpu().numpy() - ref_lse).max())
+    _say(f"{name}: max|out-ref| = {eo:.3e}  max|lse-ref| = {el:.3e}  (tol {tol:g})")
+    assert eo <= tol and el <= tol
+
+
+CASES = [
+    ("fp32_T128_G4_d64_L3", "fp32", 1, 128, 4, 1, 64, 3),
+    ("bf16_T300_G4_d128_L5", "bf16", 1, 300, 8, 2, 128, 5),
+    ("bf16_B2_T97_G3_d128_L4", "bf16", 2, 97, 6, 2, 128, 4),
+    ("bf16_T130_G32_d64_L6", "bf16", 1, 130, 32, 1, 64, 6),
+    ("fp32_T77_G2_d128_L7", "fp32", 1, 77, 4, 2, 128, 7),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fwd_q8_parity(case):
+    name, dtype, B, T, Hq, Hkv, d, L = case
+    _say(f"fwd q8 {name}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L, dtype=dtype, seed=70 + T)
+    kd, vd = _with_zero_rows(kd, vd)
+    out, lse = _run(q, ks, vs, kd, vd)
+    ref_out, ref_lse = moda_forward(np32(q), np32(ks), np32(vs), _deq_logical(kd), _deq_logical(vd))
+    _check(name, q.dtype, out, lse, ref_out, ref_lse)
+
+
+def test_fwd_q8_without_depth_is_fwd():
+    q, ks, vs, kd, vd = make_inputs(1, 100, 4, 2, 128, 0, dtype="bf16", seed=3)
+    _say("fwd q8 with L_d = 0")
+    o1, l1 = _run(q, ks, vs, kd, vd)
+    o2, l2 = moda.moda_fwd(q.cuda(), ks.cuda(), vs.cuda(), None, None, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["bf16_B1_T4096_Hq16_Hkv2_d128_L24", "bf16_B1_T65536_Hq16_Hkv2_d128_L24"])
+def test_fwd_q8_workload(name):
+    w = workload(name)
+    _say(f"fwd q8 workload {name}")
+    q, ks, vs, kd, vd = make_inputs(w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"], dtype=w["dtype"],
+                                    seed=w["seed"])
+    out, lse = _run(q, ks, vs, kd, vd)
+    if w["T"] <= 4096:
+        rows = None
+    else:
+        rows = sample_rows(w["B"], w["T"], w["Hq"], n=1024, seed=w["seed"] + 17)
+    dk, dv = _deq_logical(kd), _deq_logical(vd)
+    if rows is None:
+        ref_out, ref_lse = moda_forward(np32(q), np32(ks), np32(vs), dk, dv)
+        _check(name, q.dtype, out, lse, ref_out, ref_lse)
+    else:
+        ref_out, ref_lse = moda_forward(np32(q), np32(ks), np32(vs), dk, dv, rows=rows)
+        r = np.asarray(rows)
+        o = out[torch.from_numpy(r[:, 0]).cuda(), torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 2]).cuda()]
+        l = lse[torch.from_numpy(r[:, 0]).cuda(), torch.from_numpy(r[:, 2]).cuda(), torch.from_numpy(r[:, 1]).cuda()]
+        _check(name + " (sampled)", q.dtype, o, l, ref_out, ref_lse)
