@@ -659,8 +659,10 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
 //     barrier per block); rows of the GQA fold are gathered by per-lane
 //     offsets, rows past the end read as zeros.
 //   * One copy of each block serves both products: row-major reads for
-//     S = Q K^T and dP = dO V^T, and LDS transpose reads (ds_read_b64_tr_b16)
-//     for the Q^T and dO^T operands of dK^T and dV^T.  The 16-byte chunk index
+//     S = Q K^T and dP = dO V^T, and LDS transpose reads (ds_read_b64_tr_b16,
+//     through the compiler builtin; the two stages are separate arrays, so
+//     reads of one are not held back by loads in flight into the other) for
+//     the Q^T and dO^T operands of dK^T and dV^T.  The 16-byte chunk index
 //     is XOR-swizzled with 4 (row & 3) + ((row >> 2) & 3), which keeps both
 //     access patterns free of bank conflicts: any 16 consecutive rows get 16
 //     distinct chunks (row reads), and any 4 consecutive rows get 4 distinct
@@ -671,72 +673,6 @@ namespace bwdbf16 {
 
 // physical 16-byte chunk of logical chunk c in row r of a block
 __device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-
-// Sixteen LDS transpose reads: the four Q^T and the four dO^T operand
-// fragments of one 16-row chunk (rows +0 and +4 per fragment half), waited
-// for inside the block.
-template <int OFFQ, int OFFO>
-__device__ __forceinline__ void tr_read_qo(const uint32_t (&a)[8], bf16x8 (&fq)[4], bf16x8 (&fo)[4]) {
-  s16x4 r[16];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]),
-        "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "i"(OFFQ), "i"(OFFO)
-      : "memory");
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const s16x4 pq[2] = {r[2 * dt], r[2 * dt + 1]};
-    const s16x4 po[2] = {r[8 + 2 * dt], r[8 + 2 * dt + 1]};
-    fq[dt] = *reinterpret_cast<const bf16x8*>(pq);
-    fo[dt] = *reinterpret_cast<const bf16x8*>(po);
-  }
-}
-
-// Eight LDS transpose reads: the four K^T operand fragments of one 16-key
-// chunk, waited for inside the block.
-template <int OFF>
-__device__ __forceinline__ void tr_read8(const uint32_t (&a)[8], bf16x8 (&f)[4]) {
-  s16x4 r[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "i"(OFF)
-      : "memory");
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const s16x4 pr[2] = {r[2 * dt], r[2 * dt + 1]};
-    f[dt] = *reinterpret_cast<const bf16x8*>(pr);
-  }
-}
 
 // lane-constant LDS byte offsets of the transpose reads of a 16-row chunk of a
 // swizzled [rows][128] bf16 block: 16-lane group q16, lane j16 reads row
@@ -777,7 +713,10 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   constexpr int LOADS = QB * D / 8 / (NW * 64);   // 16-byte loads per lane per tensor per block
   constexpr uint32_t OOB = 0x80000000u;         // an offset past every buffer's range: reads zeros
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // the two stages as separate arrays, so that loads from one provably do not
+  // alias the direct-to-LDS writes in flight into the other
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -830,7 +769,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
 
   // block of rows [Rb, Rb + 64) -> stage st
   auto load_block = [&](int Rb, int st) {
-    char* sb = smem + st * STAGE;
+    char* sb = st ? smem1 : smem0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int sp = i * NW + wave;             // 4-row span of the block
@@ -857,10 +796,8 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   uint32_t roff[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(qperm * 256 + (((2 * kc + hh) ^ swz(qperm)) * 16));
-  uint32_t ta0[8], ta1[8];   // transpose-read addresses in stage 0 and stage 1
-  tr_offsets(lane, lds_addr(smem), ta0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ta1[i] = ta0[i] + STAGE;
+  uint32_t tro[8];   // transpose-read byte offsets within a block
+  tr_offsets(lane, 0u, tro);
 
   const float sl2 = p.scale_log2;
   const int rb0 = kt0 * G / QB * QB;            // first block with a row at position >= kt0
@@ -871,7 +808,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   // S - lse*sqrt(d) and dp holds dP - Delta.  The lane's 16 rows are two runs
   // of 8: sub*32 + 16c + 8hh + (0..7).
   auto products = [&]<int ST, int sub>(f32x16& s, f32x16& dp) {
-    const char* sb = smem + ST * STAGE;
+    const char* sb = ST ? smem1 : smem0;
     bf16x8 qa[NKC], oa[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -919,17 +856,20 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   };
   // dV^T += dO^T P and dK^T += Q^T dS over one sub-block
   auto update = [&]<int ST, int sub>(const bf16x8 (&pf)[2], const bf16x8 (&df)[2]) {
-    bf16x8 fq[NDT], fo[NDT];
+    const char* sb = ST ? smem1 : smem0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      if (c == 0)
-        tr_read_qo<sub * 32 * 256, OFF_O + sub * 32 * 256>(ST ? ta1 : ta0, fq, fo);
-      else
-        tr_read_qo<sub * 32 * 256 + 4096, OFF_O + sub * 32 * 256 + 4096>(ST ? ta1 : ta0, fq, fo);
+      const char* qb = sb + sub * 32 * 256 + c * 4096;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        dv[dt] = mma16(fo[dt], pf[c], dv[dt]);
-        dk[dt] = mma16(fq[dt], df[c], dk[dt]);
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + tro[2 * dt]));
+        const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + tro[2 * dt + 1]));
+        const s16x4 o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + OFF_O + tro[2 * dt]));
+        const s16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + OFF_O + tro[2 * dt + 1]));
+        const s16x4 pq[2] = {q0, q1}, po[2] = {o0, o1};
+        dv[dt] = mma16(*reinterpret_cast<const bf16x8*>(po), pf[c], dv[dt]);
+        dk[dt] = mma16(*reinterpret_cast<const bf16x8*>(pq), df[c], dk[dt]);
       }
     }
   };
@@ -1010,7 +950,10 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   constexpr int STAGE = 2 * TILE_B;
   constexpr int LOADS = BN * D / 8 / (NW * 64);
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // the two stages as separate arrays (loads from one provably do not alias
+  // the direct-to-LDS writes in flight into the other)
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1077,7 +1020,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   };
   auto load_block = [&](int blk, int st) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, blk), rv = block_rsrc(vbase, blk);
-    char* sb = smem + st * STAGE;
+    char* sb = st ? smem1 : smem0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       dma16(rk, off[i], sb + (i * NW + wave) * 1024);
@@ -1089,13 +1032,13 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   uint32_t roff[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(key_row * 256 + (((2 * kc + hh) ^ swz(key_row)) * 16));
-  uint32_t ta[8];
-  tr_offsets(lane, lds_addr(smem), ta);
+  uint32_t tro[8];   // transpose-read byte offsets within a block
+  tr_offsets(lane, 0u, tro);
 
   auto block = [&]<int ST>(int j) {
     if (j + 1 < nblocks) load_block(j + 1, ST ^ 1);
     if (wave_active && j * BN <= tw_max) {
-      const char* sb = smem + ST * STAGE;
+      const char* sb = ST ? smem1 : smem0;
       auto half = [&]<int H>() {
         bf16x8 ka[NKC], va[NKC];
 #pragma unroll
@@ -1116,13 +1059,18 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
           const float pr = __builtin_amdgcn_exp2f(key <= t_row ? __builtin_fmaf(s[r], sl2, -lse2) : -INFINITY);
           dsf[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dlt));
         }
-        bf16x8 kt[NDT];
-        tr_read8<ST * STAGE + H * 32 * 256>(ta, kt);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma16(kt[dt], dsf[0], acc[dt]);
-        tr_read8<ST * STAGE + H * 32 * 256 + 16 * 256>(ta, kt);
+        for (int c = 0; c < 2; ++c) {
+          const char* kb = sb + H * 32 * 256 + c * 16 * 256;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma16(kt[dt], dsf[1], acc[dt]);
+          for (int dt = 0; dt < NDT; ++dt) {
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + tro[2 * dt]));
+            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + tro[2 * dt + 1]));
+            const s16x4 pr[2] = {r0, r1};
+            acc[dt] = mma16(*reinterpret_cast<const bf16x8*>(pr), dsf[c], acc[dt]);
+          }
+        }
       };
       half.template operator()<0>();
       half.template operator()<1>();
