@@ -50,33 +50,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Eight LDS transpose reads (two per 32-row tile of O^T over d = 128) that
-// form the four V^T operand fragments of one 16-key chunk, completed before
-// returning (the wait is inside the same asm block, so no read is in flight
-// when the compiler next touches these registers).  a[dt] is this lane's
-// byte address of its first row for tile dt; the second row is 4 rows
-// (1024 bytes) further.
-template <int OFF>
-__device__ __forceinline__ void tr_read_chunk(const uint32_t (&a)[4], bf16x8 (&f)[4]) {
-  s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + 1024)
-      : "memory");
-  const s16x4 p0[2] = {r0, r1}, p1[2] = {r2, r3}, p2[2] = {r4, r5}, p3[2] = {r6, r7};
-  f[0] = *reinterpret_cast<const bf16x8*>(p0);
-  f[1] = *reinterpret_cast<const bf16x8*>(p1);
-  f[2] = *reinterpret_cast<const bf16x8*>(p2);
-  f[3] = *reinterpret_cast<const bf16x8*>(p3);
+// One V^T operand fragment through two LDS transpose reads
+// (ds_read_b64_tr_b16): p is this lane's byte address of its first row; the
+// second row is 4 rows (1024 bytes) further.  Each read hands the lane four
+// consecutive rows (keys) of one column (head dimension).
+__device__ __forceinline__ bf16x8 tr_frag(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
+  const s16x4 pr[2] = {r0, r1};
+  return *reinterpret_cast<const bf16x8*>(pr);
 }
 
 template <int D>
@@ -91,8 +74,16 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   constexpr int TILE = BN * D;            // elements of one K (or V) block
   constexpr int LOADS = TILE / 8 / (NW * 64);   // 16-byte loads per thread per block
 
-  // K stages 0,1 then V stages 0,1; each [BN][D], swizzled
-  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
+  // Each K stage as two 32-row halves and each V stage as one array, all
+  // separate objects: in every block the loads in flight go to (K stage ST,
+  // half 0), (K stage ST^1, half 1) and V stage ST^1 while the reads come from
+  // the other three, so the compiler can see that no read waits for them.
+  __shared__ __attribute__((aligned(1024))) bf16 smemK00[TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK01[TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK10[TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK11[TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemV0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 smemV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,16 +158,21 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         (void*)(reinterpret_cast<const char*>(head) + (long long)blk * BN * row_bytes), (short)0, bytes,
         kBufferWord3);
   };
-  // load slots [i0, i1) of block blk; slot i covers span i*NW + wave
-  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int i0, int i1) {
+  // load slots [i0, i1) of block blk; slot i covers span i*NW + wave, which
+  // lands at span (i*NW + wave - sp0) of lbase
+  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int i0, int i1,
+                      int sp0) {
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
 #pragma unroll
-    for (int i = i0; i < i1; ++i) dma16(rs, off[i], lbase + (i * NW + wave) * 512);
+    for (int i = i0; i < i1; ++i) dma16(rs, off[i], lbase + (i * NW + wave - sp0) * 512);
   };
   const int klast = nblocks - 1;
   auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
-  auto kst = [&](int st) { return smem + st * TILE; };
-  auto vst = [&](int st) { return smem + (2 + st) * TILE; };
+  // K stage st, half h (rows 32h .. 32h+31 of the block)
+  auto khalf = [&](int st, int h) -> bf16* {
+    return st ? (h ? smemK11 : smemK10) : (h ? smemK01 : smemK00);
+  };
+  auto vst = [&](int st) { return st ? smemV1 : smemV0; };
 
   // Lane-constant LDS byte offsets.
   //  K operand row r = pi(n) of a 32-row half: chunk (2kc + hh) ^ (r & 15);
@@ -190,19 +186,18 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   //  c16 + 8*(q16/2) + j16/4 (+4), logical chunk 4dt + 2(q16&1) + (j16&3)/2,
   //  half (j16&1); the swizzle XORs the chunk with 4*(row & 3) = 4*(j16/4).
   const int q16 = lane >> 4, j16 = lane & 15;
-  const uint32_t smem_base = lds_addr(smem);
-  uint32_t va[NDT];
+  uint32_t va[NDT];   // byte offsets within a V block (second row of a fragment: +1024)
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     const int r = 8 * (q16 >> 1) + (j16 >> 2);
     const int chunk = (4 * dt + 2 * (q16 & 1) + ((j16 & 3) >> 1)) ^ (4 * (j16 >> 2));
-    va[dt] = smem_base + (uint32_t)(r * D + chunk * 8 + (j16 & 1) * 4) * 2u;
+    va[dt] = (uint32_t)(r * D + chunk * 8 + (j16 & 1) * 4) * 2u;
   }
   const float sl2 = p.scale_log2;
 
   // S^T of one 32-key half-block (rows h*32.. of K stage ST) x this wave's 32 rows
   auto qk = [&]<int ST, int H>(float (&s)[16]) {
-    const char* kb0 = reinterpret_cast<const char*>(smem) + (ST * TILE + H * 32 * D) * 2;
+    const char* kb0 = reinterpret_cast<const char*>(khalf(ST, H));
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
@@ -261,14 +256,12 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   // O += P V over one 32-key half-block H of V stage ST
   auto pv = [&]<int ST, int H>(const bf16x8 (&pf)[2]) {
-    constexpr int base = ((2 + ST) * TILE + H * 32 * D) * 2;
-    bf16x8 vf[4];
-    tr_read_chunk<base>(va, vf);
+    const char* vb = reinterpret_cast<const char*>(ST ? smemV1 : smemV0) + H * 32 * D * 2;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[0], o[dt]);
-    tr_read_chunk<base + 16 * D * 2>(va, vf);
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[1], o[dt]);
+      for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = mma16(tr_frag(vb + c * 16 * D * 2 + va[dt]), pf[c], o[dt]);
   };
 
   auto rescale = [&](float alpha) {
@@ -277,9 +270,10 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   };
 
   // ---- prologue: K(0) both halves, K(1) first half, V(0) ----
-  dma_rows(kbase, 0, offk, kst(0), 0, LOADS);
-  dma_rows(kbase, clampb(1), offk, kst(1), 0, LOADS / 2);
-  dma_rows(vbase, 0, offv, vst(0), 0, LOADS);
+  dma_rows(kbase, 0, offk, khalf(0, 0), 0, LOADS / 2, 0);
+  dma_rows(kbase, 0, offk, khalf(0, 1), LOADS / 2, LOADS, 8);
+  dma_rows(kbase, clampb(1), offk, khalf(1, 0), 0, LOADS / 2, 0);
+  dma_rows(vbase, 0, offv, vst(0), 0, LOADS, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   float s_a[16], s_b[16];
@@ -293,9 +287,9 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   //   half 0: s_b = QK(K(j) rows 32-63) while softmax(s_a); P.V with V(j) rows 0-31
   //   half 1: s_a = QK(K(j+1) rows 0-31) while softmax(s_b); P.V with V(j) rows 32-63
   auto block = [&]<bool MASKED, int ST>(int j) {
-    dma_rows(kbase, clampb(j + 2), offk, kst(ST), 0, LOADS / 2);
-    dma_rows(kbase, clampb(j + 1), offk, kst(ST ^ 1), LOADS / 2, LOADS);
-    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, LOADS);
+    dma_rows(kbase, clampb(j + 2), offk, khalf(ST, 0), 0, LOADS / 2, 0);
+    dma_rows(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1), LOADS / 2, LOADS, 8);
+    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, LOADS, 0);
     bf16x8 pf[2];
     float alpha;
     bool need;
@@ -332,10 +326,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
     // the stages are free after the last barrier of the sweep: wave w uses
     // 32 rows (8 KB) at row 32 w of the first stage pair for its depth values
-    bf16* vwave = smem + wave * 32 * D;
-    uint32_t vaw[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vaw[dt] = va[dt] + (uint32_t)(wave * 32 * D * 2);
+    bf16* vwave = khalf(wave >> 1, wave & 1);
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};
@@ -396,13 +387,11 @@ void moda_fwd_bf16_kernel(FwdParams p) {
           st16(vwave + r * D + (((lane & 15) ^ (4 * (r & 3))) * 8), vr[i]);
         }
       }
-      bf16x8 vf[4];
-      tr_read_chunk<0>(vaw, vf);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[0], o[dt]);
-      tr_read_chunk<16 * D * 2>(vaw, vf);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[dt], pf[1], o[dt]);
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = mma16(tr_frag(reinterpret_cast<const char*>(vwave) + c * 16 * D * 2 + va[dt]), pf[c], o[dt]);
     }
   }
 
