@@ -67,8 +67,13 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
   }
-  if (p.L_d > 0)
-    hipLaunchKernelGGL((moda::moda_bwd_depth_kernel<E, D>), dim3((unsigned)((long long)p.T * BH)), dim3(256), 0, s, p);
+  if (p.L_d > 0) {
+    // whole positions per 32-row wave (G divides 32): the matrix-core depth kernel
+    if (sizeof(E) == 2 && D == 128 && 32 % p.G == 0)
+      hipLaunchKernelGGL((moda::moda_bwd_depth_bf16_kernel<128>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((moda::moda_bwd_depth_kernel<E, D>), dim3((unsigned)((long long)p.T * BH)), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

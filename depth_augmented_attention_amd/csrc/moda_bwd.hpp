@@ -1094,4 +1094,174 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   if (row_ok) dq_store<bf16, D>(p, b, t_row, hq, hh, acc);
 }
 
+// ---------------------------------------------------------------------------
+// bf16, d = 128, G dividing 32: depth-slot gradients on the matrix cores.
+// A wave owns 32 folded rows, i.e. 32 / G whole positions, so every depth slot
+// of those positions is seen only by this wave's rows: the wave stages its
+// rows of q and dO in its own LDS region (swizzled as in the dK/dV kernel) and
+// sweeps the 32-key tiles of the packed depth buffers that hold its
+// positions' slots -- S = Q K_d^T and dP = dO V_d^T with a lane per key (the
+// accumulators seeded with -lse*sqrt(d) and -Delta), P and dS masked to
+// "same position, slot in the window", then dV_d^T += dO^T P and
+// dK_d^T += Q^T dS -- and writes the keys of its own positions in the logical
+// [B,T,L_d,Hkv,d] layout.  No barriers: each wave touches only its own LDS.
+template <int D>
+__global__ __launch_bounds__(256) void moda_bwd_depth_bf16_kernel(BwdParams p) {
+  static_assert(D == 128, "built for head size 128");
+  using namespace bwdbf16;
+  constexpr int NW = 4;
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int REG = 32 * D * 2;                 // bytes of one wave's 32 rows
+
+  __shared__ __attribute__((aligned(1024))) char sQ[NW * REG];
+  __shared__ __attribute__((aligned(1024))) char sO[NW * REG];
+  __shared__ __attribute__((aligned(16))) float sL[NW * 32];
+  __shared__ __attribute__((aligned(16))) float sD[NW * 32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int tile = (int)(blockIdx.x / BH);
+  const int b = bh / p.Hkv;
+  const int kvh = bh % p.Hkv;
+  const int G = p.G, T = p.T, Hq = p.Hq;
+  const int TG = T * G;
+  const int Rw = tile * (NW * 32) + wave * 32;
+  if (Rw >= TG) return;
+  const int tw_min = div_g(Rw, p.g_magic, p.g_shift);
+  const int tw_max = div_g((Rw + 31 < TG ? Rw + 31 : TG - 1), p.g_magic, p.g_shift);
+
+  char* wq = sQ + wave * REG;
+  char* wo = sO + wave * REG;
+  float* wl = sL + wave * 32;
+  float* wd = sD + wave * 32;
+  {
+    const bf16* qg = reinterpret_cast<const bf16*>(p.q);
+    const bf16* og = reinterpret_cast<const bf16*>(p.dO);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), lc = lane & 15;
+      const int R = Rw + r;
+      u32x4 qv = {0, 0, 0, 0}, ov = {0, 0, 0, 0};
+      if (R < TG) {
+        const int t = div_g(R, p.g_magic, p.g_shift);
+        const long long off = (((long long)b * T + t) * Hq + kvh * G + (R - t * G)) * D + lc * 8;
+        qv = ld16(qg + off);
+        ov = ld16(og + off);
+      }
+      st16(wq + r * 256 + ((lc ^ swz(r)) * 16), qv);
+      st16(wo + r * 256 + ((lc ^ swz(r)) * 16), ov);
+    }
+    if (lane < 32) {
+      const int R = Rw + lane;
+      float l = 0.f, dl = 0.f;
+      if (R < TG) {
+        const int t = div_g(R, p.g_magic, p.g_shift);
+        const long long li = ((long long)b * Hq + kvh * G + (R - t * G)) * T + t;
+        l = p.work[p.BHT + li];     // -lse * sqrt(d)
+        dl = p.work[li];            // -Delta
+      }
+      wl[lane] = l;
+      wd[lane] = dl;
+    }
+  }
+
+  const int qperm = key_row_perm(n);
+  uint32_t roff[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) roff[kc] = (uint32_t)(qperm * 256 + (((2 * kc + hh) ^ swz(qperm)) * 16));
+  uint32_t tro[8];
+  tr_offsets(lane, 0u, tro);
+  const float sl2 = p.scale_log2, sc = p.scale;
+  const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+  const bf16* kdb = reinterpret_cast<const bf16*>(p.kd) + (long long)bh * p.NKp * D;
+  const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
+  const long long nlo = (long long)tw_min * L_cap + slot_lo;
+  const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
+
+  for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+    if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
+    const long long key = n0 + n;
+    const int tk = (int)(key / L_cap);
+    const int slot = (int)(key - (long long)tk * L_cap) - slot_lo;
+    const bool key_ok = tk < T && slot >= 0 && slot < L_d;
+    const int r_lo = tk * G;                      // rows [r_lo, r_lo + G) sit at position tk
+    bf16x8 kf[NKC], vf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      kf[kc] = load_frag(kdb + key * D + kc * 16 + hh * 8);
+      vf[kc] = load_frag(vdb + key * D + kc * 16 + hh * 8);
+    }
+    f32x16 s, dp;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4* lp = reinterpret_cast<const f32x4*>(wl + 16 * c + 8 * hh);
+      const f32x4* dpp = reinterpret_cast<const f32x4*>(wd + 16 * c + 8 * hh);
+      const f32x4 la = lp[0], lb = lp[1], da = dpp[0], db = dpp[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[8 * c + j] = la[j];
+        s[8 * c + 4 + j] = lb[j];
+        dp[8 * c + j] = da[j];
+        dp[8 * c + 4 + j] = db[j];
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      s = mma16(*reinterpret_cast<const bf16x8*>(wq + roff[kc]), kf[kc], s);
+      dp = mma16(*reinterpret_cast<const bf16x8*>(wo + roff[kc]), vf[kc], dp);
+    }
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * c + j;
+        const int R = Rw + 16 * c + 8 * hh + j;
+        const float x = (key_ok && R >= r_lo && R < r_lo + G) ? s[r] * sl2 : -INFINITY;
+        const float pr = __builtin_amdgcn_exp2f(x);
+        pf[c][j] = (bf16)pr;
+        df[c][j] = (bf16)(pr * dp[r]);
+      }
+    f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const char* qb = wq + c * 16 * 256;
+        const char* ob = wo + c * 16 * 256;
+        const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + tro[2 * dt]));
+        const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + tro[2 * dt + 1]));
+        const s16x4 o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ob + tro[2 * dt]));
+        const s16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ob + tro[2 * dt + 1]));
+        const s16x4 pq[2] = {q0, q1}, po[2] = {o0, o1};
+        dv[dt] = mma16(*reinterpret_cast<const bf16x8*>(po), pf[c], dv[dt]);
+        dk[dt] = mma16(*reinterpret_cast<const bf16x8*>(pq), df[c], dk[dt]);
+      }
+    if (key_ok && tk >= tw_min && tk <= tw_max) {
+      const long long orow = ((((long long)b * T + tk) * L_d + slot) * p.Hkv + kvh) * D;
+      bf16* dkp = reinterpret_cast<bf16*>(p.dkd) + orow;
+      bf16* dvp = reinterpret_cast<bf16*>(p.dvd) + orow;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int e = dt * 32 + g4 * 8 + hh * 4;
+          store4(dkp + e, dk[dt][g4 * 4 + 0] * sc, dk[dt][g4 * 4 + 1] * sc, dk[dt][g4 * 4 + 2] * sc,
+                 dk[dt][g4 * 4 + 3] * sc);
+          store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
+        }
+    }
+  }
+}
+
 }  // namespace moda
