@@ -138,3 +138,25 @@ def test_fwd_q8_workload(name):
         o = out[torch.from_numpy(r[:, 0]).cuda(), torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 2]).cuda()]
         l = lse[torch.from_numpy(r[:, 0]).cuda(), torch.from_numpy(r[:, 2]).cuda(), torch.from_numpy(r[:, 1]).cuda()]
         _check(name + " (sampled)", q.dtype, o, l, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64), ("bf16", 64)])
+def test_fwd_q8_bitwise_on_exact_codes(dtype, d):
+    """Depth values that are integer multiples (|k| <= 127, row max 127) of a
+    power of two quantise exactly, so the 8-bit forward must give bit for bit
+    the output of the plain forward on the same values."""
+    _say(f"fwd q8 exact codes {dtype} d={d}")
+    B, T, Hq, Hkv, L = 1, 150, 8, 2, 5
+    q, ks, vs, _, _ = make_inputs(B, T, Hq, Hkv, d, 0, dtype=dtype, seed=11)
+    g = torch.Generator().manual_seed(12)
+    td = q.dtype
+    codes = torch.randint(-127, 128, (2, B, T, L, Hkv, d), generator=g)
+    codes[..., 0] = 127
+    kd = (codes[0].float() * 2.0 ** -6).to(td)
+    vd = (codes[1].float() * 2.0 ** -5).to(td)
+    dev = torch.device("cuda:0")
+    o1, l1 = _run(q, ks, vs, kd, vd)
+    kp, vp = moda.moda_pack_depth(kd.to(dev), vd.to(dev))
+    o2, l2 = moda.moda_fwd(q.to(dev), ks.to(dev), vs.to(dev), kp, vp, L)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
