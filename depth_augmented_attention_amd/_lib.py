@@ -40,7 +40,7 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -c 'import __graft_entry__ as g; g.build()')")
+            "(python -m depth_augmented_attention_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
     c_int, c_vp = ctypes.c_int, ctypes.c_void_p
     lib.moda_depth_packed_elems.argtypes = [c_int] * 5

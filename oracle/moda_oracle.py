@@ -27,7 +27,7 @@ What is computed (exact attention, evaluated in float64):
     * gist.science (de), same section, Group-Aware Indexing: GQA, several
       query heads share one KV head.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
     * the formula's Q K_i^T terms are taken before masking; the depth mask
       restricts them to position t;
     * the causal mask includes s = t ("itself and earlier");

@@ -103,11 +103,12 @@ def test_bwd_workload_T4096_all_elements():
     _check_all(w["name"], q.dtype, got, ref)
 
 
-def test_bwd_workload_T65536_sampled():
-    """At the benchmark size: the query and depth-slot gradients of sampled
+@pytest.mark.parametrize("name", ["bf16_B1_T65536_Hq16_Hkv2_d128_L24", "bf16_B1_T65536_Hq32_Hkv1_d128_L48"])
+def test_bwd_workload_T65536_sampled(name):
+    """At the 64K workloads: the query and depth-slot gradients of sampled
     (b, t, kv head) groups against the oracle's per-group form, and the exact
     sums (sum of dv over all keys = sum of dout; sum of dk = 0) per kv head."""
-    w = workload("bf16_B1_T65536_Hq16_Hkv2_d128_L24")
+    w = workload(name)
     _say(f"bwd {w['name']} (sampled groups + gradient sums)")
     B, T, Hq, Hkv, d, L_d = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
     q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype=w["dtype"], seed=w["seed"])
