@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the write-step and depth-window measurements")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the depth-overhead sweep over the other bf16 workloads")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
@@ -307,6 +309,46 @@ def main():
         if "fwd_ms_L0" in res:
             res["q8_overhead_vs_L0"] = q8_fwd_ms / res["fwd_ms_L0"] - 1.0
         del packed
+
+    if not args.no_sweep:
+        # overhead of the depth slots on the other bf16 workloads (G and depth
+        # sweep): forward with depth vs the same kernel at L_d = 0, inputs N(0,1)
+        # drawn on the GPU (timing only)
+        from moda_inputs import WORKLOADS
+        sweep = {}
+        for ws in WORKLOADS:
+            if ws["dtype"] != "bf16" or ws["name"] == w["name"]:
+                continue
+            log(f"sweep {ws['name']}")
+            sB, sT, sHq, sHkv, sd, sL = ws["B"], ws["T"], ws["Hq"], ws["Hkv"], ws["d"], ws["L_d"]
+            g = torch.Generator(device=dev).manual_seed(ws["seed"])
+            rn = lambda *sh: torch.randn(*sh, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            sq, sk, sv = rn(sB, sT, sHq, sd), rn(sB, sT, sHkv, sd), rn(sB, sT, sHkv, sd)
+            skd, svd = rn(sB, sT, sL, sHkv, sd), rn(sB, sT, sL, sHkv, sd)
+            skp, svp = moda.moda_pack_depth(skd, svd)
+            so = torch.empty_like(sq)
+            sl = torch.empty(sB, sHq, sT, dtype=torch.float32, device=dev)
+            reps = 20 if sT <= 16384 else 5
+
+            def timed(Ld, kp_, vp_):
+                moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl)
+                torch.cuda.synchronize()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                e[0].record()
+                for i in range(reps):
+                    moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl)
+                    e[i + 1].record()
+                torch.cuda.synchronize()
+                ts = sorted(e[i].elapsed_time(e[i + 1]) for i in range(reps))
+                return ts[len(ts) // 2]                       # median
+
+            t_d = timed(sL, skp, svp)
+            t_0 = timed(0, None, None)
+            Fs = useful_flops(sB, sT, sHq, sd, sL)
+            sweep[ws["name"]] = {"fwd_ms": t_d, "fwd_ms_L0": t_0, "overhead_vs_L0": t_d / t_0 - 1.0,
+                                 "fwd_tflops": Fs / (t_d * 1e-3) / 1e12, "reps": reps}
+            del sq, sk, sv, skd, svd, skp, svp, so, sl
+        res["overhead_sweep"] = sweep
 
     if not args.no_bwd:
         # backward of the same forward: dq, dk/dv of sequence and depth keys
