@@ -15,10 +15,13 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     depth_packed_elems,
     moda_append_depth,
+    moda_append_depth_q8,
     moda_bwd,
+    moda_bwd_window,
     moda_fwd,
     moda_fwd_q8,
     moda_fwd_window,
+    moda_fwd_window_q8,
     moda_pack_depth,
     moda_pack_depth_q8,
 )

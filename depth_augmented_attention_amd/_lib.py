@@ -19,8 +19,8 @@ MODA_ERR_HIP = 5
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
-           "moda_append_depth", "moda_bwd", "moda_pack_depth_q8", "moda_fwd_q8",
-           "moda_status_string")
+           "moda_append_depth", "moda_bwd", "moda_bwd_window", "moda_pack_depth_q8", "moda_fwd_q8",
+           "moda_fwd_window_q8", "moda_append_depth_q8", "moda_status_string")
 
 
 class ModaError(RuntimeError):
@@ -59,6 +59,12 @@ def load() -> ctypes.CDLL:
     lib.moda_pack_depth_q8.restype = c_int
     lib.moda_fwd_q8.argtypes = [c_vp] * 9 + [c_int] * 7 + [c_vp]
     lib.moda_fwd_q8.restype = c_int
+    lib.moda_bwd_window.argtypes = [c_vp] * 14 + [c_int] * 9 + [c_vp]
+    lib.moda_bwd_window.restype = c_int
+    lib.moda_fwd_window_q8.argtypes = [c_vp] * 9 + [c_int] * 9 + [c_vp]
+    lib.moda_fwd_window_q8.restype = c_int
+    lib.moda_append_depth_q8.argtypes = [c_vp] * 6 + [c_int] * 7 + [c_vp]
+    lib.moda_append_depth_q8.restype = c_int
     lib.moda_status_string.argtypes = [c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -165,6 +165,39 @@ int moda_fwd_window(const void* q, const void* k_seq, const void* v_seq, const v
                   L_cap, slot_lo, slot_hi, dtype, stream);
 }
 
+int moda_fwd_window_q8(const void* q, const void* k_seq, const void* v_seq, const int8_t* k_q,
+                       const int8_t* v_q, const float* k_scale, const float* v_scale, void* out,
+                       float* lse, int B, int T, int Hq, int Hkv, int d, int L_cap, int slot_lo,
+                       int slot_hi, int dtype, void* stream) {
+  return fwd_impl(q, k_seq, v_seq, k_q, v_q, k_scale, v_scale, 1, out, lse, B, T, Hq, Hkv, d, L_cap,
+                  slot_lo, slot_hi, dtype, stream);
+}
+
+int moda_append_depth_q8(const void* k_new, const void* v_new, int8_t* k_q, int8_t* v_q,
+                         float* k_scale, float* v_scale, int B, int T, int Hkv, int d, int L_cap,
+                         int slot, int dtype, void* stream) {
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_cap < 1) return MODA_ERR_SHAPE;
+  if (slot < 0 || slot >= L_cap) return MODA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
+  if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !k_q || !v_q || !k_scale || !v_scale) return MODA_ERR_NULL;
+  moda::AppendQ8Params p{k_new, v_new, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_cap, slot,
+                         padded_depth_keys(T, L_cap)};
+  const long long rows = (long long)B * T * Hkv;
+  const long long rpb = 256 / (d / 8);
+  const long long grid = (rows + rpb - 1) / rpb;
+  if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == MODA_BF16) {
+    if (d == 128) hipLaunchKernelGGL((moda::moda_append_depth_q8_kernel<moda::bf16, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((moda::moda_append_depth_q8_kernel<moda::bf16, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((moda::moda_append_depth_q8_kernel<float, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((moda::moda_append_depth_q8_kernel<float, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  }
+  return hipGetLastError() == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
 int moda_fwd_q8(const void* q, const void* k_seq, const void* v_seq, const int8_t* k_q,
                 const int8_t* v_q, const float* k_scale, const float* v_scale, void* out, float* lse,
                 int B, int T, int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
@@ -227,16 +260,19 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
-int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
-             const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
-             void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B, int T,
-             int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
-  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_d < 0) return MODA_ERR_SHAPE;
+static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+                    void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
+                    int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
+                    void* stream) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
+  if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
   if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || !work)
     return MODA_ERR_NULL;
+  const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
@@ -252,10 +288,10 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   p.o = out; p.dO = dout; p.lse = lse; p.work = work; p.BHT = (long long)B * Hq * T;
   p.dq = dq; p.dk = dk_seq; p.dv = dv_seq; p.dkd = dk_depth; p.dvd = dv_depth;
   p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
-  p.L_d = L_d; p.L_cap = L_d > 0 ? L_d : 1; p.slot_lo = 0;
+  p.L_d = L_d; p.L_cap = L_cap > 0 ? L_cap : 1; p.slot_lo = slot_lo;
   p.ntiles = (int)ntiles;
   p.nktiles = (int)nktiles;
-  p.NKp = padded_depth_keys(T, L_d);
+  p.NKp = padded_depth_keys(T, L_cap);
   p.scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   {
@@ -273,6 +309,24 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   else
     e = d == 128 ? launch_bwd<float, 128>(p, s) : launch_bwd<float, 64>(p, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+}
+
+int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+             const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+             void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B, int T,
+             int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, dq, dk_seq, dv_seq, dk_depth,
+                  dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
+}
+
+int moda_bwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                    const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+                    void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
+                    int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
+                    void* stream) {
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, dq, dk_seq, dv_seq, dk_depth,
+                  dv_depth, work, B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, dtype, stream);
 }
 
 }  // extern "C"

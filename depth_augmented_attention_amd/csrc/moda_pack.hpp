@@ -144,25 +144,20 @@ __device__ __forceinline__ u32x2 quantize8(const float (&x)[8], float scale) {
   return w;
 }
 
+// Quantise one row of K and one row of V (D elements each) with LPR = D / 8
+// lanes per row, 8 elements per lane: the row maximum is reduced across the
+// row's lanes (every lane of the wave takes part in the exchange), then codes
+// and scales are written when `valid`.  Rows with valid == false but
+// store == true are padding: scale 0, codes 0.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p) {
-  constexpr int LPR = D / 8;                    // lanes per packed row
-  constexpr int RPB = 256 / LPR;                // rows per workgroup
-  const long long rows = (long long)p.B * p.Hkv * p.NKp;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int l = threadIdx.x % LPR;
+__device__ __forceinline__ void quant_rows(const E* srck, const E* srcv, bool load, bool store, int l,
+                                           int8_t* dk, int8_t* dv, float* sk_out, float* sv_out) {
+  constexpr int LPR = D / 8;
   float xk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (row < rows) {
-    const long long bh = row / p.NKp;
-    const int n = (int)(row % p.NKp);
-    if (n < p.T * p.L_d) {
-      const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
-      const int t = n / p.L_d, j = n - t * p.L_d;
-      const long long src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D + l * 8;
-      load8(reinterpret_cast<const E*>(p.kd) + src, xk);
-      load8(reinterpret_cast<const E*>(p.vd) + src, xv);
-    }
+  if (load) {
+    load8(srck + l * 8, xk);
+    load8(srcv + l * 8, xv);
   }
   float mk = 0.f, mv = 0.f;
 #pragma unroll
@@ -173,14 +168,70 @@ __global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p)
     mv = fmaxf(mv, __shfl_xor(mv, off));
   }
   const float sk = mk / 127.f, sv = mv / 127.f;
-  if (row < rows) {
-    *reinterpret_cast<u32x2*>(p.kq + row * D + l * 8) = quantize8(xk, sk);
-    *reinterpret_cast<u32x2*>(p.vq + row * D + l * 8) = quantize8(xv, sv);
+  if (store) {
+    *reinterpret_cast<u32x2*>(dk + l * 8) = quantize8(xk, sk);
+    *reinterpret_cast<u32x2*>(dv + l * 8) = quantize8(xv, sv);
     if (l == 0) {
-      p.ks[row] = sk;
-      p.vs[row] = sv;
+      *sk_out = sk;
+      *sv_out = sv;
     }
   }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p) {
+  constexpr int LPR = D / 8;                    // lanes per packed row
+  constexpr int RPB = 256 / LPR;                // rows per workgroup
+  const long long rows = (long long)p.B * p.Hkv * p.NKp;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int l = threadIdx.x % LPR;
+  bool load = false;
+  long long src = 0;
+  if (row < rows) {
+    const long long bh = row / p.NKp;
+    const int n = (int)(row % p.NKp);
+    if (n < p.T * p.L_d) {
+      const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
+      const int t = n / p.L_d, j = n - t * p.L_d;
+      src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D;
+      load = true;
+    }
+  }
+  const long long r = row < rows ? row : 0;
+  quant_rows<E, D>(reinterpret_cast<const E*>(p.kd) + src, reinterpret_cast<const E*>(p.vd) + src, load,
+                   row < rows, l, p.kq + r * D, p.vq + r * D, p.ks + r, p.vs + r);
+}
+
+// Write step with 8-bit depth KV: one layer's K/V rows quantised into slot
+// `slot` of int8 packed buffers with L_cap slots per position (same codes as
+// moda_pack_depth_q8_kernel would give those rows).
+struct AppendQ8Params {
+  const void* k_new;
+  const void* v_new;
+  int8_t* kq;
+  int8_t* vq;
+  float* ks;
+  float* vs;
+  int B, T, Hkv, L_cap, slot;
+  long long NKp;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void moda_append_depth_q8_kernel(AppendQ8Params p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const long long rows = (long long)p.B * p.T * p.Hkv;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, t, kvh) in input order
+  const int l = threadIdx.x % LPR;
+  const bool ok = row < rows;
+  const long long r = ok ? row : 0;
+  const int kvh = (int)(r % p.Hkv);
+  const long long bt = r / p.Hkv;
+  const int t = (int)(bt % p.T);
+  const int b = (int)(bt / p.T);
+  const long long dst = ((long long)b * p.Hkv + kvh) * p.NKp + (long long)t * p.L_cap + p.slot;
+  quant_rows<E, D>(reinterpret_cast<const E*>(p.k_new) + r * D, reinterpret_cast<const E*>(p.v_new) + r * D,
+                   ok, ok, l, p.kq + dst * D, p.vq + dst * D, p.ks + dst, p.vs + dst);
 }
 
 }  // namespace moda

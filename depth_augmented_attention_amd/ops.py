@@ -163,6 +163,18 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     L_d == 0.  `grads` may supply those five output tensors; `work` a float32
     [2,B,Hq,T] scratch tensor.
     """
+    return moda_bwd_window(q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, dout,
+                           grads=grads, work=work, stream=stream)
+
+
+def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+                    k_depth: torch.Tensor | None, v_depth: torch.Tensor | None,
+                    L_cap: int, slot_lo: int, slot_hi: int,
+                    out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                    grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
+    """Gradients of moda_fwd_window(..., L_cap, slot_lo, slot_hi): as
+    moda_bwd, with the depth gradients of slots slot_lo .. slot_hi-1
+    ([B,T,slot_hi-slot_lo,Hkv,d])."""
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
     B, T, Hq, d = q.shape
@@ -179,23 +191,25 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq"), (out, "out"), (lse, "lse"),
                     (dout, "dout")):
         _dev(t, name)
+    L_d = slot_hi - slot_lo
     kd_ptr = vd_ptr = None
     if L_d > 0:
         if k_depth is None or v_depth is None:
-            raise ValueError("packed depth buffers are required when L_d > 0")
-        n = depth_packed_elems(B, T, Hkv, d, L_d)
+            raise ValueError("packed depth buffers are required when slots are read")
+        n = depth_packed_elems(B, T, Hkv, d, L_cap)
         for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
             _dev(t, name)
             if t.numel() != n or t.dtype != q.dtype:
                 raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
         kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
-    shapes = [(B, T, Hq, d), (B, T, Hkv, d), (B, T, Hkv, d), (B, T, L_d, Hkv, d), (B, T, L_d, Hkv, d)]
+    Ld = max(L_d, 0)
+    shapes = [(B, T, Hq, d), (B, T, Hkv, d), (B, T, Hkv, d), (B, T, Ld, Hkv, d), (B, T, Ld, Hkv, d)]
     if grads is None:
         grads = tuple(torch.empty(s, dtype=q.dtype, device=q.device) if (i < 3 or L_d > 0) else None
                       for i, s in enumerate(shapes))
     grads = tuple(grads)
     for i, (g, s) in enumerate(zip(grads, shapes)):
-        if i >= 3 and L_d == 0:
+        if i >= 3 and L_d <= 0:
             continue
         if g is None or tuple(g.shape) != s or g.dtype != q.dtype:
             raise ValueError(f"gradient {i} must be {q.dtype} {s}")
@@ -206,11 +220,11 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     if work.dtype != torch.float32 or work.shape != (2, B, Hq, T):
         raise ValueError("work must be float32 [2,B,Hq,T]")
     ptr = [g.data_ptr() if g is not None else None for g in grads]
-    st = load().moda_bwd(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
-                         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
-                         ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_d, _dtype_code(q),
-                         _stream(stream))
-    check(st, "moda_bwd")
+    st = load().moda_bwd_window(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+                                out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+                                ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi,
+                                _dtype_code(q), _stream(stream))
+    check(st, "moda_bwd_window")
     return grads
 
 
@@ -237,10 +251,39 @@ def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None
     return kq, vq, ks, vs
 
 
-def moda_fwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8, L_d: int,
-                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                with_lse: bool = True, stream=None):
-    """MoDA forward over 8-bit depth KV (the four buffers of moda_pack_depth_q8)."""
+def _check_q8(packed_q8, B, T, Hkv, d, L_cap):
+    kq, vq, ks, vs = packed_q8
+    n = depth_packed_elems(B, T, Hkv, d, L_cap)
+    for t, name, dt, cnt in ((kq, "k_q", torch.int8, n), (vq, "v_q", torch.int8, n),
+                             (ks, "k_scale", torch.float32, n // d), (vs, "v_scale", torch.float32, n // d)):
+        _dev(t, name)
+        if t.dtype != dt or t.numel() != cnt:
+            raise ValueError(f"{name} must hold {cnt} elements of {dt}")
+    return [kq.data_ptr(), vq.data_ptr(), ks.data_ptr(), vs.data_ptr()]
+
+
+def moda_append_depth_q8(k_new: torch.Tensor, v_new: torch.Tensor, packed_q8, L_cap: int, slot: int,
+                         stream=None):
+    """Write step into 8-bit packed buffers (the four of moda_pack_depth_q8
+    built with L_cap slots per position), in place."""
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must both be [B,T,Hkv,d] of one dtype")
+    B, T, Hkv, d = k_new.shape
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, name)
+    ptrs = _check_q8(packed_q8, B, T, Hkv, d, L_cap)
+    st = load().moda_append_depth_q8(k_new.data_ptr(), v_new.data_ptr(), *ptrs, B, T, Hkv, d, L_cap, slot,
+                                     _dtype_code(k_new), _stream(stream))
+    check(st, "moda_append_depth_q8")
+    return packed_q8
+
+
+def moda_fwd_window_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8,
+                       L_cap: int, slot_lo: int, slot_hi: int,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       with_lse: bool = True, stream=None):
+    """MoDA forward over depth slots [slot_lo, slot_hi) of 8-bit packed
+    buffers with L_cap slots per position."""
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
     B, T, Hq, d = q.shape
@@ -251,16 +294,7 @@ def moda_fwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packe
         raise ValueError("q, k_seq, v_seq must share one dtype")
     for t, name in ((q, "q"), (k_seq, "k_seq"), (v_seq, "v_seq")):
         _dev(t, name)
-    ptrs = [None] * 4
-    if L_d > 0:
-        kq, vq, ks, vs = packed_q8
-        n = depth_packed_elems(B, T, Hkv, d, L_d)
-        for t, name, dt, cnt in ((kq, "k_q", torch.int8, n), (vq, "v_q", torch.int8, n),
-                                 (ks, "k_scale", torch.float32, n // d), (vs, "v_scale", torch.float32, n // d)):
-            _dev(t, name)
-            if t.dtype != dt or t.numel() != cnt:
-                raise ValueError(f"{name} must hold {cnt} elements of {dt}")
-        ptrs = [kq.data_ptr(), vq.data_ptr(), ks.data_ptr(), vs.data_ptr()]
+    ptrs = _check_q8(packed_q8, B, T, Hkv, d, L_cap) if slot_hi > slot_lo else [None] * 4
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out")
@@ -270,8 +304,16 @@ def moda_fwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packe
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
-    st = load().moda_fwd_q8(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs, out.data_ptr(),
-                            lse.data_ptr() if lse is not None else None, B, T, Hq, Hkv, d, L_d,
-                            _dtype_code(q), _stream(stream))
-    check(st, "moda_fwd_q8")
+    st = load().moda_fwd_window_q8(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs, out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, B, T, Hq, Hkv, d, L_cap,
+                                   slot_lo, slot_hi, _dtype_code(q), _stream(stream))
+    check(st, "moda_fwd_window_q8")
     return out, lse
+
+
+def moda_fwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8, L_d: int,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                with_lse: bool = True, stream=None):
+    """MoDA forward over 8-bit depth KV (the four buffers of moda_pack_depth_q8)."""
+    return moda_fwd_window_q8(q, k_seq, v_seq, packed_q8, L_d, 0, L_d, out=out, lse=lse,
+                              with_lse=with_lse, stream=stream)

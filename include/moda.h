@@ -239,6 +239,48 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq,
              int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
              void* stream);
 
+/*
+ * moda_bwd_window -- moda_bwd for the forward moda_fwd_window(..., L_cap,
+ * slot_lo, slot_hi, ...): the packed buffers hold L_cap slots per position and
+ * the gradients of slots slot_lo .. slot_hi-1 are written to dk_depth /
+ * dv_depth, logical [B, T, slot_hi - slot_lo, Hkv, d] (NULL iff the window is
+ * empty).  Other arguments as for moda_bwd; moda_bwd(..., L_d, ...) is
+ * moda_bwd_window(..., L_cap = L_d, 0, L_d, ...).
+ */
+int moda_bwd_window(const void* q, const void* k_seq, const void* v_seq,
+                    const void* k_depth, const void* v_depth,
+                    const void* out, const float* lse, const void* dout,
+                    void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+                    float* work,
+                    int B, int T, int Hq, int Hkv, int d,
+                    int L_cap, int slot_lo, int slot_hi, int dtype,
+                    void* stream);
+
+/*
+ * moda_fwd_window_q8 -- moda_fwd_window over 8-bit depth KV: the codes and
+ * scales of a buffer with L_cap slots per position (moda_pack_depth_q8 with
+ * L_d = L_cap, or moda_append_depth_q8), reading slots slot_lo .. slot_hi-1.
+ */
+int moda_fwd_window_q8(const void* q, const void* k_seq, const void* v_seq,
+                       const int8_t* k_q, const int8_t* v_q,
+                       const float* k_scale, const float* v_scale,
+                       void* out, float* lse,
+                       int B, int T, int Hq, int Hkv, int d,
+                       int L_cap, int slot_lo, int slot_hi, int dtype,
+                       void* stream);
+
+/*
+ * moda_append_depth_q8 -- the write step into 8-bit packed buffers: one
+ * layer's K/V [B, T, Hkv, d] quantised (as moda_pack_depth_q8 does each row)
+ * into slot `slot` of int8 buffers with L_cap slots per position and their
+ * row scales.  0 <= slot < L_cap.  Appending slots 0 .. L-1 into zero-filled
+ * buffers gives bit for bit what moda_pack_depth_q8 produces for L slots.
+ */
+int moda_append_depth_q8(const void* k_new, const void* v_new,
+                         int8_t* k_q, int8_t* v_q, float* k_scale, float* v_scale,
+                         int B, int T, int Hkv, int d, int L_cap, int slot, int dtype,
+                         void* stream);
+
 /* Static, human-readable name of a moda_status value. */
 const char* moda_status_string(int status);
 

@@ -159,3 +159,19 @@ def test_q8_validation():
     assert lib.moda_fwd_q8(*args, None, FAKE, FAKE, None, 1, 4, 2, 1, 128, 3, 1, None) == _lib.MODA_ERR_NULL
     assert lib.moda_fwd_q8(*args, FAKE, FAKE, FAKE, None, 1, 4, 3, 2, 128, 3, 1, None) == _lib.MODA_ERR_SHAPE
     assert lib.moda_fwd_q8(*args, FAKE, FAKE, FAKE, None, 1, 4, 2, 1, 128, -1, 1, None) == _lib.MODA_ERR_SHAPE
+
+
+def test_window_q8_and_bwd_window_validation():
+    lib = moda.load()
+    a5 = (FAKE,) * 5
+    # fwd_window_q8: window past the capacity, missing scales
+    assert lib.moda_fwd_window_q8(*a5, FAKE, FAKE, FAKE, None, 1, 4, 2, 1, 128, 4, 0, 5, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_fwd_window_q8(*a5, None, FAKE, FAKE, None, 1, 4, 2, 1, 128, 4, 1, 3, 1, None) == _lib.MODA_ERR_NULL
+    # append_q8: slot out of range, NULL scale
+    assert lib.moda_append_depth_q8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 128, 3, 3, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth_q8(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 128, 3, 1, 1, None) == _lib.MODA_ERR_NULL
+    # bwd_window: empty window allows NULL depth pointers; a bad window is rejected
+    ptrs = [FAKE] * 14
+    assert lib.moda_bwd_window(*ptrs, 1, 4, 2, 1, 128, 4, 3, 2, 1, None) == _lib.MODA_ERR_SHAPE
+    ptrs[11] = None
+    assert lib.moda_bwd_window(*ptrs, 1, 4, 2, 1, 128, 4, 1, 3, 1, None) == _lib.MODA_ERR_NULL

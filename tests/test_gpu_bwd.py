@@ -137,3 +137,23 @@ def test_bwd_workload_T65536_sampled(name):
     _say(f"{w['name']}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
     for k, v in errs.items():
         assert v <= tol, f"{k} error {v} > {tol}"
+
+
+@pytest.mark.parametrize("case", [("bf16", 1, 180, 8, 2, 128, 6, 2, 5), ("fp32", 1, 70, 4, 1, 64, 5, 3, 5),
+                                  ("bf16", 1, 100, 6, 2, 128, 4, 0, 4)])
+def test_bwd_window_parity(case):
+    """Backward of a depth-slot window: the oracle backward of the forward over
+    the window's slots; depth gradients are those of the window's slots."""
+    dtype, B, T, Hq, Hkv, d, L_cap, lo, hi = case
+    _say(f"bwd window {case}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_cap, dtype=dtype, seed=80 + T)
+    dout = make_dout(B, T, Hq, d, dtype=dtype, seed=80 + T)
+    dev = torch.device("cuda:0")
+    kp, vp = moda.moda_pack_depth(kd.to(dev), vd.to(dev))
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    out, lse = moda.moda_fwd_window(qd, ksd, vsd, kp, vp, L_cap, lo, hi)
+    grads = moda.moda_bwd_window(qd, ksd, vsd, kp, vp, L_cap, lo, hi, out, lse, dd)
+    torch.cuda.synchronize()
+    got = [g.double().cpu().numpy() for g in grads]
+    ref = moda_backward(np32(q), np32(ks), np32(vs), np32(kd)[:, :, lo:hi], np32(vd)[:, :, lo:hi], np32(dout))
+    _check_all(f"window {case}", q.dtype, got, ref)

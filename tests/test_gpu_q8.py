@@ -160,3 +160,37 @@ def test_fwd_q8_bitwise_on_exact_codes(dtype, d):
     o2, l2 = moda.moda_fwd(q.to(dev), ks.to(dev), vs.to(dev), kp, vp, L)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_append_q8_equals_pack_q8():
+    """Appending slots 0..L-1 one layer at a time into zero-filled 8-bit
+    buffers gives bit for bit the buffers of moda_pack_depth_q8."""
+    B, T, Hkv, d, L = 2, 45, 2, 128, 5
+    _say("append q8 vs pack q8")
+    _, _, _, kd, vd = make_inputs(B, T, Hkv, Hkv, d, L, dtype="bf16", seed=21)
+    kd, vd = _with_zero_rows(kd, vd)
+    ref = moda.moda_pack_depth_q8(kd.cuda(), vd.cuda())
+    n = moda.depth_packed_elems(B, T, Hkv, d, L)
+    buf = (torch.zeros(n, dtype=torch.int8, device="cuda"), torch.zeros(n, dtype=torch.int8, device="cuda"),
+           torch.zeros(n // d, dtype=torch.float32, device="cuda"), torch.zeros(n // d, dtype=torch.float32, device="cuda"))
+    for j in range(L):
+        moda.moda_append_depth_q8(kd[:, :, j].contiguous().cuda(), vd[:, :, j].contiguous().cuda(), buf, L, j)
+    torch.cuda.synchronize()
+    for a, b in zip(buf, ref):
+        assert torch.equal(a.view(torch.int8) if a.dtype == torch.int8 else a.view(torch.int32),
+                           b.view(torch.int8) if b.dtype == torch.int8 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", [("bf16", 1, 200, 8, 2, 128, 6, 2, 5), ("fp32", 1, 90, 4, 1, 64, 4, 0, 4),
+                                  ("bf16", 2, 70, 4, 2, 64, 8, 7, 8)])
+def test_fwd_window_q8_parity(case):
+    dtype, B, T, Hq, Hkv, d, L_cap, lo, hi = case
+    _say(f"fwd window q8 {case}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_cap, dtype=dtype, seed=90 + T)
+    dev = torch.device("cuda:0")
+    packed = moda.moda_pack_depth_q8(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd_window_q8(q.to(dev), ks.to(dev), vs.to(dev), packed, L_cap, lo, hi)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = moda_forward(np32(q), np32(ks), np32(vs), _deq_logical(kd)[:, :, lo:hi],
+                                    _deq_logical(vd)[:, :, lo:hi])
+    _check(f"window q8 {case}", q.dtype, out, lse, ref_out, ref_lse)
