@@ -13,8 +13,14 @@ namespace {
 
 constexpr int kWaves = 4;          // waves per workgroup of the forward kernels
 
-// query rows per workgroup of the kernel that serves (dtype, d)
-int rows_per_tile(int, int) { return 32 * kWaves; }
+// Waves per workgroup of the forward for (dtype, d, shape): the bf16 d = 128
+// kernel takes 8 waves (256 rows) when that still gives at least two
+// workgroups per compute unit of a 256-CU GPU, else 4 (128 rows) like the
+// generic kernel.
+int fwd_waves(int dtype, int d, long long rows, long long BH) {
+  if (dtype == MODA_BF16 && d == 128 && (rows + 255) / 256 * BH >= 512) return 8;
+  return kWaves;
+}
 
 bool valid_dtype(int dtype) { return dtype == MODA_F32 || dtype == MODA_BF16; }
 bool supported_d(int d) { return d == 64 || d == 128; }
@@ -25,11 +31,15 @@ long long padded_depth_keys(int T, int L_d) {
 }
 
 template <typename E, int D>
-hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, hipStream_t s) {
-  if constexpr (sizeof(E) == 2 && D == 128)
-    hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D>), dim3(grid), dim3(kWaves * 64), 0, s, p);
-  else
+hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, int nw, hipStream_t s) {
+  if constexpr (sizeof(E) == 2 && D == 128) {
+    if (nw == 8)
+      hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 8>), dim3(grid), dim3(8 * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 4>), dim3(grid), dim3(4 * 64), 0, s, p);
+  } else {
     hipLaunchKernelGGL((moda::moda_fwd_kernel<E, D, kWaves>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -134,7 +144,8 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   if (L_d > 0 && q8 && (!k_scale || !v_scale)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
-  const int tile_rows = rows_per_tile(dtype, d);
+  const int nw = fwd_waves(dtype, d, rows, (long long)B * Hkv);
+  const int tile_rows = 32 * nw;
   const long long ntiles = (rows + tile_rows - 1) / tile_rows;
   const long long grid = ntiles * B * Hkv;
   if (grid > 0x7fffffffLL || rows > 0x7fffffffLL) return MODA_ERR_SHAPE;
@@ -152,9 +163,9 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == MODA_BF16)
-    e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)grid, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, s);
+    e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)grid, nw, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, nw, s);
   else
-    e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, s) : launch_fwd<float, 64>(p, (unsigned)grid, s);
+    e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, nw, s) : launch_fwd<float, 64>(p, (unsigned)grid, nw, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 

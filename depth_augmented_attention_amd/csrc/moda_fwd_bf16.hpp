@@ -17,7 +17,11 @@
 //     XOR swizzle of the 16-byte chunk index (K: chunk ^ (row & 15);
 //     V: chunk ^ 4 * (row & 3)), chosen so that every 16-lane K read and every
 //     32-lane transposed V read touches 64 distinct banks.
-//   * At most 256 registers per wave, so two workgroups share a compute unit.
+//   * Eight waves (256 query rows) per workgroup and at most 256 registers per
+//     wave: two waves per SIMD, and each K/V block staged in LDS serves 256
+//     rows (one workgroup per compute unit; +3% over four-wave workgroups
+//     with two per compute unit).  Grids too small to fill the GPU twice over
+//     with 256-row tiles use four-wave workgroups (128 rows) instead.
 //   * Probabilities are taken against the running max without forming the
 //     block's row max first; only when a lane's sum of them exceeds 2^8 (a
 //     score rose well above the max, or the first block) is the row max
@@ -62,17 +66,19 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* p) {
   return *reinterpret_cast<const bf16x8*>(pr);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup (32 query rows each): 8, or 4 for small grids.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moda_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 128, "the bf16 fast path is built for head size 128");
-  constexpr int NW = 4;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   constexpr int BN = 64;                  // keys per sequence block
   constexpr int NKC = D / 16;             // 16-wide k-chunks over d
   constexpr int NDT = D / 32;             // 32-row tiles of O^T over d
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TILE = BN * D;            // elements of one K (or V) block
-  constexpr int LOADS = TILE / 8 / (NW * 64);   // 16-byte loads per thread per block
+  constexpr int SPANS = TILE / 512;        // 1 KB spans per block
+  constexpr int LOADS = (SPANS + NW - 1) / NW;
 
   // Each K stage as two 32-row halves and each V stage as one array, all
   // separate objects: in every block the loads in flight go to (K stage ST,
@@ -158,13 +164,16 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         (void*)(reinterpret_cast<const char*>(head) + (long long)blk * BN * row_bytes), (short)0, bytes,
         kBufferWord3);
   };
-  // load slots [i0, i1) of block blk; slot i covers span i*NW + wave, which
+  // load spans [s_lo, s_hi) of block blk; slot i covers span i*NW + wave, which
   // lands at span (i*NW + wave - sp0) of lbase
-  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int i0, int i1,
+  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int s_lo, int s_hi,
                       int sp0) {
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
 #pragma unroll
-    for (int i = i0; i < i1; ++i) dma16(rs, off[i], lbase + (i * NW + wave - sp0) * 512);
+    for (int i = 0; i < LOADS; ++i) {
+      const int sp = i * NW + wave;
+      if (sp >= s_lo && sp < s_hi) dma16(rs, off[i], lbase + (sp - sp0) * 512);
+    }
   };
   const int klast = nblocks - 1;
   auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
@@ -270,10 +279,10 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   };
 
   // ---- prologue: K(0) both halves, K(1) first half, V(0) ----
-  dma_rows(kbase, 0, offk, khalf(0, 0), 0, LOADS / 2, 0);
-  dma_rows(kbase, 0, offk, khalf(0, 1), LOADS / 2, LOADS, 8);
-  dma_rows(kbase, clampb(1), offk, khalf(1, 0), 0, LOADS / 2, 0);
-  dma_rows(vbase, 0, offv, vst(0), 0, LOADS, 0);
+  dma_rows(kbase, 0, offk, khalf(0, 0), 0, 8, 0);
+  dma_rows(kbase, 0, offk, khalf(0, 1), 8, 16, 8);
+  dma_rows(kbase, clampb(1), offk, khalf(1, 0), 0, 8, 0);
+  dma_rows(vbase, 0, offv, vst(0), 0, 16, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   float s_a[16], s_b[16];
@@ -287,9 +296,9 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   //   half 0: s_b = QK(K(j) rows 32-63) while softmax(s_a); P.V with V(j) rows 0-31
   //   half 1: s_a = QK(K(j+1) rows 0-31) while softmax(s_b); P.V with V(j) rows 32-63
   auto block = [&]<bool MASKED, int ST>(int j) {
-    dma_rows(kbase, clampb(j + 2), offk, khalf(ST, 0), 0, LOADS / 2, 0);
-    dma_rows(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1), LOADS / 2, LOADS, 8);
-    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, LOADS, 0);
+    dma_rows(kbase, clampb(j + 2), offk, khalf(ST, 0), 0, 8, 0);
+    dma_rows(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1), 8, 16, 8);
+    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, 16, 0);
     bf16x8 pf[2];
     float alpha;
     bool need;
@@ -324,9 +333,11 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
     const bf16* kdb = reinterpret_cast<const bf16*>(p.kd) + (long long)bh * p.NKp * D;
     const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
-    // the stages are free after the last barrier of the sweep: wave w uses
-    // 32 rows (8 KB) at row 32 w of the first stage pair for its depth values
-    bf16* vwave = khalf(wave >> 1, wave & 1);
+    // the stages are free after the last barrier of the sweep: each wave takes
+    // 32 rows (8 KB) of them -- the four K halves, then the halves of the two
+    // V stages -- for its depth values
+    bf16* vwave = wave < 4 ? khalf(wave >> 1, wave & 1) : ((wave < 6 ? smemV0 : smemV1) + (wave & 1) * 32 * D);
+    static_assert(NW <= 8, "one 8 KB region per wave in the 64 KB of stages");
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
       f32x16 acc = f32x16{};

@@ -71,6 +71,9 @@ EDGE = [
     ("fp32", 2, 65, 3, 1, 64, 4),      # G = 3
     ("bf16", 1, 300, 64, 1, 128, 2),   # G = 64 > 32 rows of a wave
     ("fp32", 1, 130, 4, 1, 64, 0),     # depth-free float32 with a ragged last block
+    # grids large enough for the eight-wave (256-row) bf16 tiles, ragged tails
+    ("bf16", 4, 1100, 32, 16, 128, 3), # G = 2, 9 tiles of 256 rows x 64 (b, kv head)
+    ("bf16", 2, 2100, 64, 16, 128, 5), # G = 4, ragged last tile, L_d * T not a multiple of 32
 ]
 
 
