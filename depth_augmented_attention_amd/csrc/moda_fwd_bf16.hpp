@@ -12,7 +12,9 @@
 //   * V stays key-major in LDS; the P.V product reads it with the LDS
 //     transpose load (ds_read_b64_tr_b16), which hands each lane four
 //     consecutive keys of one head dimension -- the operand order the matrix
-//     cores want -- without any shuffles.
+//     cores want -- without any shuffles.  A half-block's V fragments are
+//     read before its softmax starts, so the LDS latency is spent under the
+//     vector work instead of in front of each P.V product.
 //   * LDS rows are 256 bytes with no padding; bank conflicts are avoided by an
 //     XOR swizzle of the 16-byte chunk index (K: chunk ^ (row & 15);
 //     V: chunk ^ 4 * (row & 3)), chosen so that every 16-lane K read and every
@@ -263,14 +265,21 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     return need;
   };
 
-  // O += P V over one 32-key half-block H of V stage ST
-  auto pv = [&]<int ST, int H>(const bf16x8 (&pf)[2]) {
+  // V^T operand fragments of one 32-key half-block H of V stage ST, read ahead
+  // of the softmax whose probabilities they multiply
+  auto vload = [&]<int ST, int H>(bf16x8 (&vf)[2 * NDT]) {
     const char* vb = reinterpret_cast<const char*>(ST ? smemV1 : smemV0) + H * 32 * D * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        o[dt] = mma16(tr_frag(vb + c * 16 * D * 2 + va[dt]), pf[c], o[dt]);
+      for (int dt = 0; dt < NDT; ++dt) vf[c * NDT + dt] = tr_frag(vb + c * 16 * D * 2 + va[dt]);
+  };
+  // O += P V
+  auto pv = [&](const bf16x8 (&vf)[2 * NDT], const bf16x8 (&pf)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = mma16(vf[c * NDT + dt], pf[c], o[dt]);
   };
 
   auto rescale = [&](float alpha) {
@@ -299,17 +308,19 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     dma_rows(kbase, clampb(j + 2), offk, khalf(ST, 0), 0, 8, 0);
     dma_rows(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1), 8, 16, 8);
     dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, 16, 0);
-    bf16x8 pf[2];
+    bf16x8 pf[2], vf[2 * NDT];
     float alpha;
     bool need;
+    vload.template operator()<ST, 0>(vf);
     qk.template operator()<ST, 1>(s_b);
     need = softmax.template operator()<MASKED>(s_a, j * BN, pf, alpha);
     if (need) rescale(alpha);
-    pv.template operator()<ST, 0>(pf);
+    pv(vf, pf);
+    vload.template operator()<ST, 1>(vf);
     qk.template operator()<ST ^ 1, 0>(s_a);
     need = softmax.template operator()<MASKED>(s_b, j * BN + 32, pf, alpha);
     if (need) rescale(alpha);
-    pv.template operator()<ST, 1>(pf);
+    pv(vf, pf);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
