@@ -95,7 +95,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 31;
   const int hh = lane >> 5;
 
@@ -351,27 +351,69 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     static_assert(NW <= 8, "one 8 KB region per wave in the 64 KB of stages");
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
-      f32x16 acc = f32x16{};
+      // K operand fragments (rows n0 + key_row) and this lane's share of the
+      // 32 value rows (row n0 + 4 i + lane / 16, chunk lane % 16), loaded
+      // together: one round trip to memory per tile
+      bf16x8 kfr[NKC];
+      u32x4 vr[8];
       if (p.q8) {
-        const long long kr = (long long)bh * p.NKp + n0 + key_row;
-        const int8_t* krow = reinterpret_cast<const int8_t*>(p.kd) + kr * D + hh * 8;
-        const float ks = p.ksc[kr];
+        // tile base (wave-uniform) plus 32-bit lane offsets
+        const long long r0 = (long long)bh * p.NKp + n0;
+        const int8_t* kt = reinterpret_cast<const int8_t*>(p.kd) + r0 * D;
+        const int8_t* vt = reinterpret_cast<const int8_t*>(p.vd) + r0 * D;
+        const float* kst = p.ksc + r0;
+        const float* vst_ = p.vsc + r0;
+        u32x2 kc8[NKC], vc8[8];
+        float vs[8];
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) acc = mma16(dequant_frag_bf16(krow + kc * 16, ks), qf[kc], acc);
+        for (int kc = 0; kc < NKC; ++kc)
+          kc8[kc] = *reinterpret_cast<const u32x2*>(kt + (uint32_t)(key_row * D + hh * 8 + kc * 16));
+        const float ks = kst[key_row];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 4 * i + (lane >> 4);
+          vc8[i] = *reinterpret_cast<const u32x2*>(vt + (uint32_t)(r * D + (lane & 15) * 8));
+          vs[i] = vst_[r];
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) kfr[kc] = dequant_frag_bf16(reinterpret_cast<const int8_t*>(&kc8[kc]), ks);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8 f = dequant_frag_bf16(reinterpret_cast<const int8_t*>(&vc8[i]), vs[i]);
+          vr[i] = *reinterpret_cast<const u32x4*>(&f);
+        }
       } else {
-        const bf16* krow = kdb + (n0 + key_row) * D + hh * 8;
+        // tile base (wave-uniform) plus 32-bit lane offsets
+        const bf16* kt = kdb + n0 * D;
+        const bf16* vt = vdb + n0 * D;
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) acc = mma16(load_frag(krow + kc * 16), qf[kc], acc);
+        for (int kc = 0; kc < NKC; ++kc) kfr[kc] = load_frag(kt + (uint32_t)(key_row * D + hh * 8 + kc * 16));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vr[i] = ld16(vt + (uint32_t)((4 * i + (lane >> 4)) * D + (lane & 15) * 8));
+      }
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) acc = mma16(kfr[kc], qf[kc], acc);
+      // the value rows go to this wave's LDS region with the V-stage swizzle,
+      // to be read back with the same transpose reads as the sequence blocks
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        st16(vwave + r * D + (((lane & 15) ^ (4 * (r & 3))) * 8), vr[i]);
       }
       // same arithmetic as a sequence half-block: masked raw scores, one FMA
       // into exp2; the max is exact here (these tiles are few) and the sum is
       // taken over the bf16-rounded probabilities that enter P.V
       float sv[16];
-      const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
-      const long long own_hi = own_lo + L_d;
+      // this row's window relative to the tile (small: the wave's rows span a
+      // few positions around the tile)
+      // (key reg_key(i, hh) = 16 (i >> 3) + 8 hh + (i & 7): the lane's 8 hh
+      // moves to the bounds, so that each register compares with a constant)
+      const int own_lo = (int)((long long)t_row * L_cap + slot_lo - n0) - 8 * hh;
+      const int own_hi = own_lo + L_d;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = reg_key(i, hh);
+        const int key = 16 * (i >> 3) + (i & 7);
         sv[i] = (key >= own_lo && key < own_hi) ? acc[i] : -INFINITY;
       }
       float mx = sv[0];
@@ -387,28 +429,6 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       }
       bf16x8 pf[2];
       l_run += exps(sv, -m_run, pf);
-      // V^T operand through this wave's LDS region: the 32 key-major value
-      // rows with the V-stage swizzle, then the same transpose reads as the
-      // sequence blocks
-      {
-        u32x4 vr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const long long row = n0 + 4 * i + (lane >> 4);
-          if (p.q8) {
-            const long long r = (long long)bh * p.NKp + row;
-            const bf16x8 f = dequant_frag_bf16(reinterpret_cast<const int8_t*>(p.vd) + r * D + (lane & 15) * 8, p.vsc[r]);
-            vr[i] = *reinterpret_cast<const u32x4*>(&f);
-          } else {
-            vr[i] = ld16(vdb + row * D + (lane & 15) * 8);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 4 * i + (lane >> 4);
-          st16(vwave + r * D + (((lane & 15) ^ (4 * (r & 3))) * 8), vr[i]);
-        }
-      }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
