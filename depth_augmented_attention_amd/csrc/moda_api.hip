@@ -17,8 +17,9 @@ constexpr int kWaves = 4;          // waves per workgroup of the forward kernels
 // kernel takes 8 waves (256 rows) when that still gives at least two
 // workgroups per compute unit of a 256-CU GPU, else 4 (128 rows) like the
 // generic kernel.
+constexpr long long kCUs = 256;     // compute units of an MI355X
 int fwd_waves(int dtype, int d, long long rows, long long BH) {
-  if (dtype == MODA_BF16 && d == 128 && (rows + 255) / 256 * BH >= 512) return 8;
+  if (dtype == MODA_BF16 && d == 128 && (rows + 255) / 256 * BH >= 2 * kCUs) return 8;
   return kWaves;
 }
 
@@ -157,6 +158,9 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
   p.L_d = L_d; p.L_cap = L_cap > 0 ? L_cap : 1; p.slot_lo = slot_lo;
   p.ntiles = (int)ntiles;
+  // at most two workgroups per compute unit for the whole grid: pair long
+  // tiles with short ones (with more rounds, longest first balances by itself)
+  p.paired = grid <= 2 * kCUs && B * Hkv <= kCUs && kCUs % (B * Hkv) == 0;
   p.NKp = padded_depth_keys(T, L_cap);
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
 

@@ -45,6 +45,7 @@ struct FwdParams {
   int L_cap;        // slots per position in the packed buffers (key n = t*L_cap + slot)
   int slot_lo;      // first slot read
   int ntiles;       // query tiles per (b, kvh)
+  int paired;       // tile order for grids of at most two rounds (query_tile)
   long long NKp;    // padded depth keys per (b, kvh)
   float scale_log2; // log2(e) / sqrt(d)
 };
@@ -57,6 +58,18 @@ __device__ __forceinline__ bool depth_tile_used(long long n0, int L_cap, int slo
   if (t0 != t1) return true;
   const long long w0 = t0 * L_cap + slot_lo;
   return w0 < n0 + 32 && w0 + L_d > n0;
+}
+
+// Query tile of workgroup slot s = blockIdx / (B * Hkv).  Longest tiles
+// (latest positions, most keys) first; with `paired` set (a grid that the GPU
+// runs in at most two rounds, two workgroups per compute unit) the second
+// half of the slots takes the tiles in ascending order instead, so that the
+// two workgroups that share a compute unit -- slots s and s + ntiles / 2 --
+// have lengths adding up to about the same for every compute unit.
+__device__ __forceinline__ int query_tile(int s, int ntiles, int paired) {
+  const int h = (ntiles + 1) / 2;
+  if (!paired || s < h) return ntiles - 1 - s;
+  return s - h;
 }
 
 // Online-softmax step over NV new scores (log2 units, masked ones -inf) held
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
 
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH;
-  const int tile = p.ntiles - 1 - (int)(blockIdx.x / BH);   // heaviest first
+  const int tile = query_tile((int)(blockIdx.x / BH), p.ntiles, p.paired);
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;

@@ -101,7 +101,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH;
-  const int tile = p.ntiles - 1 - (int)(blockIdx.x / BH);
+  const int tile = query_tile((int)(blockIdx.x / BH), p.ntiles, p.paired);
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;
