@@ -854,8 +854,9 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
       }
     }
   };
-  // dV^T += dO^T P and dK^T += Q^T dS over one sub-block
-  auto update = [&]<int ST, int sub>(const bf16x8 (&pf)[2], const bf16x8 (&df)[2]) {
+  // Q^T and dO^T operand fragments of one sub-block (transpose reads), read
+  // ahead of the softmax whose outputs they multiply
+  auto tload = [&]<int ST, int sub>(bf16x8 (&qt)[2 * NDT], bf16x8 (&ot)[2 * NDT]) {
     const char* sb = ST ? smem1 : smem0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -868,10 +869,21 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
         const s16x4 o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + OFF_O + tro[2 * dt]));
         const s16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + OFF_O + tro[2 * dt + 1]));
         const s16x4 pq[2] = {q0, q1}, po[2] = {o0, o1};
-        dv[dt] = mma16(*reinterpret_cast<const bf16x8*>(po), pf[c], dv[dt]);
-        dk[dt] = mma16(*reinterpret_cast<const bf16x8*>(pq), df[c], dk[dt]);
+        qt[c * NDT + dt] = *reinterpret_cast<const bf16x8*>(pq);
+        ot[c * NDT + dt] = *reinterpret_cast<const bf16x8*>(po);
       }
     }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over one sub-block
+  auto update = [&](const bf16x8 (&qt)[2 * NDT], const bf16x8 (&ot)[2 * NDT], const bf16x8 (&pf)[2],
+                    const bf16x8 (&df)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        dv[dt] = mma16(ot[c * NDT + dt], pf[c], dv[dt]);
+        dk[dt] = mma16(qt[c * NDT + dt], df[c], dk[dt]);
+      }
   };
   // all sub-blocks, the products of the next issued before the softmax of
   // the current so that matrix and vector work overlap within the wave
@@ -880,10 +892,12 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
     products.template operator()<ST, 0>(s[0], dp[0]);
     [&]<int... I>(std::integer_sequence<int, I...>) {
       ([&] {
+        bf16x8 qt[2 * NDT], ot[2 * NDT];
+        tload.template operator()<ST, I>(qt, ot);
         if constexpr (I + 1 < NSUB) products.template operator()<ST, I + 1>(s[(I + 1) & 1], dp[(I + 1) & 1]);
         bf16x8 pf[2], df[2];
         softmax.template operator()<I, MASKED>(Rb, s[I & 1], dp[I & 1], pf, df);
-        update.template operator()<ST, I>(pf, df);
+        update(qt, ot, pf, df);
       }(), ...);
     }(std::make_integer_sequence<int, NSUB>{});
   };
