@@ -136,6 +136,7 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
                     int dtype, void* stream) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
+  if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
@@ -193,6 +194,7 @@ int moda_append_depth_q8(const void* k_new, const void* v_new, int8_t* k_q, int8
                          int slot, int dtype, void* stream) {
   if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_cap < 1) return MODA_ERR_SHAPE;
   if (slot < 0 || slot >= L_cap) return MODA_ERR_SHAPE;
+  if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
   if (!k_new || !v_new || !k_q || !v_q || !k_scale || !v_scale) return MODA_ERR_NULL;
@@ -258,6 +260,7 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
                       int T, int Hkv, int d, int L_cap, int slot, int dtype, void* stream) {
   if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_cap < 1) return MODA_ERR_SHAPE;
   if (slot < 0 || slot >= L_cap) return MODA_ERR_SHAPE;
+  if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
   if (!k_new || !v_new || !k_packed || !v_packed) return MODA_ERR_NULL;
@@ -282,6 +285,7 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
                     void* stream) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
+  if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;

@@ -35,6 +35,9 @@
  *   - Supported: dtype MODA_F32 or MODA_BF16, head size d = 64 or 128,
  *     any B, T >= 1, Hkv >= 1 with Hq a multiple of Hkv (G = 1 .. Hq),
  *     L_d >= 0.  Inputs are expected to be finite.
+ *   - Packed depth keys are indexed n = t * L + slot with 31-bit integers:
+ *     every call that takes a depth count or capacity L (L_d or L_cap)
+ *     returns MODA_ERR_SHAPE when T * L exceeds 2^31 - 33.
  */
 #ifndef MODA_H
 #define MODA_H

@@ -175,3 +175,18 @@ def test_window_q8_and_bwd_window_validation():
     assert lib.moda_bwd_window(*ptrs, 1, 4, 2, 1, 128, 4, 3, 2, 1, None) == _lib.MODA_ERR_SHAPE
     ptrs[11] = None
     assert lib.moda_bwd_window(*ptrs, 1, 4, 2, 1, 128, 4, 1, 3, 1, None) == _lib.MODA_ERR_NULL
+
+
+def test_packed_key_index_bound():
+    # T * L_cap must leave the packed key index n = t * L_cap + slot (plus the
+    # padding to 32) inside 31 bits: every entry point that takes a depth
+    # capacity rejects a larger one before any HIP call
+    lib = moda.load()
+    T, cap = 1 << 20, 1 << 11                     # T * cap = 2^31
+    a = (FAKE,) * 6
+    assert lib.moda_fwd_window(*a, None, 1, T, 2, 1, 128, cap, 0, 1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_fwd_window_q8(*(FAKE,) * 8, None, 1, T, 2, 1, 128, cap, 0, 1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth(FAKE, FAKE, FAKE, FAKE, 1, T, 1, 128, cap, 0, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_append_depth_q8(*(FAKE,) * 6, 1, T, 1, 128, cap, 0, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_bwd_window(*(FAKE,) * 14, 1, T, 2, 1, 128, cap, 0, 1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_pack_depth(FAKE, FAKE, FAKE, FAKE, 1, T, 1, 128, cap, 1, None) == _lib.MODA_ERR_SHAPE
