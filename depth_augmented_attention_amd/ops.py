@@ -32,6 +32,22 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _one_device(*tensors) -> torch.device:
+    """The GPU that all (non-None) tensors of one call live on."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors of one call must be on one GPU, got {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def _call(device: torch.device, fn: str, stream, *args) -> int:
+    """Call C entry point `fn` with `device` current (the library launches on
+    the current device); the stream (default: that device's current stream)
+    is the last argument."""
+    with torch.cuda.device(device):
+        return getattr(load(), fn)(*args, _stream(stream))
+
+
 def depth_packed_elems(B: int, T: int, Hkv: int, d: int, L_d: int) -> int:
     n = load().moda_depth_packed_elems(B, T, Hkv, d, L_d)
     if n < 0:
@@ -62,9 +78,10 @@ def moda_pack_depth(k_depth: torch.Tensor, v_depth: torch.Tensor,
     if k_packed.numel() != n or v_packed.numel() != n or k_packed.dtype != k_depth.dtype \
             or v_packed.dtype != k_depth.dtype:
         raise ValueError(f"packed buffers must hold {n} elements of {k_depth.dtype}")
-    st = load().moda_pack_depth(k_depth.data_ptr(), v_depth.data_ptr(), k_packed.data_ptr(),
-                                v_packed.data_ptr(), B, T, Hkv, d, L_d, _dtype_code(k_depth),
-                                _stream(stream))
+    dev = _one_device(k_depth, v_depth, k_packed, v_packed)
+    st = _call(dev, "moda_pack_depth", stream,
+        k_depth.data_ptr(), v_depth.data_ptr(), k_packed.data_ptr(),
+        v_packed.data_ptr(), B, T, Hkv, d, L_d, _dtype_code(k_depth))
     check(st, "moda_pack_depth")
     return k_packed, v_packed
 
@@ -82,9 +99,11 @@ def moda_append_depth(k_new: torch.Tensor, v_new: torch.Tensor, k_packed: torch.
     if k_packed.numel() != n or v_packed.numel() != n or k_packed.dtype != k_new.dtype \
             or v_packed.dtype != k_new.dtype:
         raise ValueError(f"packed buffers must hold {n} elements of {k_new.dtype}")
-    st = load().moda_append_depth(k_new.data_ptr(), v_new.data_ptr(), k_packed.data_ptr(),
-                                  v_packed.data_ptr(), B, T, Hkv, d, L_cap, slot,
-                                  _dtype_code(k_new), _stream(stream))
+    dev = _one_device(k_new, v_new, k_packed, v_packed)
+    st = _call(dev, "moda_append_depth", stream,
+        k_new.data_ptr(), v_new.data_ptr(), k_packed.data_ptr(),
+        v_packed.data_ptr(), B, T, Hkv, d, L_cap, slot,
+        _dtype_code(k_new))
     check(st, "moda_append_depth")
     return k_packed, v_packed
 
@@ -141,10 +160,11 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
-    st = load().moda_fwd_window(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
-                                out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, _dtype_code(q),
-                                _stream(stream))
+    dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse)
+    st = _call(dev, "moda_fwd_window", stream,
+        q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, _dtype_code(q))
     check(st, "moda_fwd_window")
     return out, lse
 
@@ -220,10 +240,13 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     if work.dtype != torch.float32 or work.shape != (2, B, Hq, T):
         raise ValueError("work must be float32 [2,B,Hq,T]")
     ptr = [g.data_ptr() if g is not None else None for g in grads]
-    st = load().moda_bwd_window(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
-                                out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
-                                ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi,
-                                _dtype_code(q), _stream(stream))
+    dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
+                      dout, work, *grads[:3], *(grads[3:] if L_d > 0 else ()))
+    st = _call(dev, "moda_bwd_window", stream,
+        q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+        ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi,
+        _dtype_code(q))
     check(st, "moda_bwd_window")
     return grads
 
@@ -244,9 +267,11 @@ def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None
         return kq, vq, ks, vs
     for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
         _dev(t, name)
-    st = load().moda_pack_depth_q8(k_depth.data_ptr(), v_depth.data_ptr(), kq.data_ptr(), vq.data_ptr(),
-                                   ks.data_ptr(), vs.data_ptr(), B, T, Hkv, d, L_d,
-                                   _dtype_code(k_depth), _stream(stream))
+    dev = _one_device(k_depth, v_depth, kq, vq, ks, vs)
+    st = _call(dev, "moda_pack_depth_q8", stream,
+        k_depth.data_ptr(), v_depth.data_ptr(), kq.data_ptr(), vq.data_ptr(),
+        ks.data_ptr(), vs.data_ptr(), B, T, Hkv, d, L_d,
+        _dtype_code(k_depth))
     check(st, "moda_pack_depth_q8")
     return kq, vq, ks, vs
 
@@ -272,8 +297,10 @@ def moda_append_depth_q8(k_new: torch.Tensor, v_new: torch.Tensor, packed_q8, L_
     for t, name in ((k_new, "k_new"), (v_new, "v_new")):
         _dev(t, name)
     ptrs = _check_q8(packed_q8, B, T, Hkv, d, L_cap)
-    st = load().moda_append_depth_q8(k_new.data_ptr(), v_new.data_ptr(), *ptrs, B, T, Hkv, d, L_cap, slot,
-                                     _dtype_code(k_new), _stream(stream))
+    dev = _one_device(k_new, v_new, *packed_q8)
+    st = _call(dev, "moda_append_depth_q8", stream,
+        k_new.data_ptr(), v_new.data_ptr(), *ptrs, B, T, Hkv, d, L_cap, slot,
+        _dtype_code(k_new))
     check(st, "moda_append_depth_q8")
     return packed_q8
 
@@ -304,9 +331,11 @@ def moda_fwd_window_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
-    st = load().moda_fwd_window_q8(q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs, out.data_ptr(),
-                                   lse.data_ptr() if lse is not None else None, B, T, Hq, Hkv, d, L_cap,
-                                   slot_lo, slot_hi, _dtype_code(q), _stream(stream))
+    dev = _one_device(q, k_seq, v_seq, *(packed_q8 if slot_hi > slot_lo else ()), out, lse)
+    st = _call(dev, "moda_fwd_window_q8", stream,
+        q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs, out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, B, T, Hq, Hkv, d, L_cap,
+        slot_lo, slot_hi, _dtype_code(q))
     check(st, "moda_fwd_window_q8")
     return out, lse
 

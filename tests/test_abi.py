@@ -8,6 +8,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import depth_augmented_attention_amd as moda
 from depth_augmented_attention_amd import _lib
@@ -190,3 +191,13 @@ def test_packed_key_index_bound():
     assert lib.moda_append_depth_q8(*(FAKE,) * 6, 1, T, 1, 128, cap, 0, 1, None) == _lib.MODA_ERR_SHAPE
     assert lib.moda_bwd_window(*(FAKE,) * 14, 1, T, 2, 1, 128, cap, 0, 1, 1, None) == _lib.MODA_ERR_SHAPE
     assert lib.moda_pack_depth(FAKE, FAKE, FAKE, FAKE, 1, T, 1, 128, cap, 1, None) == _lib.MODA_ERR_SHAPE
+
+
+def test_binding_rejects_mixed_devices():
+    # every tensor of one call must live on one GPU: the library launches on
+    # the current device (checked in the binding before any HIP call)
+    from depth_augmented_attention_amd import ops
+    a = torch.empty(0)
+    assert ops._one_device(a, None, a) == a.device
+    with pytest.raises(ValueError):
+        ops._one_device(a, torch.empty(0, device="meta"))
