@@ -247,6 +247,13 @@ def main():
         res["fwd_tflops_L0"] = useful_flops(B, T, Hq, d, 0) / (avg_l0 * 1e-3) / 1e12
         res["overhead_vs_L0"] = avg_fwd / avg_l0 - 1.0
         res["overhead_vs_L0_with_pack"] = (avg_fwd + avg_pack) / avg_l0 - 1.0
+        # depth stream: its bytes over the time the depth slots add to the
+        # forward (above the HBM peak means the stream is hidden under the sweep)
+        depth_stream_bytes = 2.0 * B * T * L_d * Hkv * d * q.element_size()
+        res["depth_stream_bytes"] = depth_stream_bytes
+        res["depth_incremental_ms"] = avg_fwd - avg_l0
+        res["depth_stream_gbps_incremental"] = (depth_stream_bytes / ((avg_fwd - avg_l0) * 1e-3) / 1e9
+                                                if avg_fwd > avg_l0 else None)
         log(f"L_d=0 fwd {avg_l0:.3f} ms, overhead {100 * res['overhead_vs_L0']:.2f}%")
 
     if not args.no_extras and L_d > 0:
