@@ -5,10 +5,12 @@
 // and for overlapping matrix-core and vector work:
 //   * K and V blocks go from HBM straight into LDS with the direct
 //     global->LDS 16-byte loads (no staging registers, no LDS store
-//     instructions).  K runs one block ahead of V: while block j's softmax and
-//     P.V run, the scores of block j+1 are already being formed on the matrix
-//     cores, so a wave always has independent matrix and vector work.  Two LDS
-//     stages each for K and V; one workgroup barrier per block.
+//     instructions).  Scores run half a block ahead of the softmax: while
+//     the softmax and P.V of one 32-key half run, the scores of the next half
+//     are already being formed on the matrix cores, so a wave always has
+//     independent matrix and vector work (K is loaded half a block further
+//     ahead than V).  Two LDS stages each for K and V; one workgroup barrier
+//     per 64-key block.
 //   * V stays key-major in LDS; the P.V product reads it with the LDS
 //     transpose load (ds_read_b64_tr_b16), which hands each lane four
 //     consecutive keys of one head dimension -- the operand order the matrix
@@ -33,6 +35,10 @@
 //     drops the max reduction from the common path.  Row sums come from the
 //     same bf16 probabilities that feed the P.V product (v_dot2_f32_bf16).
 //   * The causal mask is only evaluated in the last few blocks of a tile.
+//   * The depth slots of a wave's positions are folded in after the sweep,
+//     one 32-key depth tile at a time, with the tile's key fragments and
+//     value rows loaded together (one round trip to memory per tile) and the
+//     values transposed through the wave's own LDS region.
 #pragma once
 
 #include "moda_common.hpp"
