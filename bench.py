@@ -93,6 +93,7 @@ def cpu_baseline(w, inputs, budget_s):
     rows = rows[rng.permutation(len(rows))]
     done = 0
     flops = 0.0
+    c0 = time.process_time()
     t0 = time.perf_counter()
     chunk = 64
     while done < len(rows) and time.perf_counter() - t0 < budget_s:
@@ -101,6 +102,7 @@ def cpu_baseline(w, inputs, budget_s):
         flops += useful_flops(w["B"], w["T"], w["Hq"], w["d"], w["L_d"], rows=sel)
         done += len(sel)
     dt = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / dt      # CPU seconds per wall second, all threads
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -109,6 +111,7 @@ def cpu_baseline(w, inputs, budget_s):
         "sample": f"{done} seeded random (b,t,h) query rows of {w['name']} "
                   f"(float64 numpy oracle, {dt:.1f} s; rate = useful FLOPs of those rows / time)",
         "rows_per_s": done / dt,
+        "cpu_seconds_per_wall_second": busy,
     }
 
 
