@@ -103,11 +103,13 @@ def test_bwd_workload_T4096_all_elements():
     _check_all(w["name"], q.dtype, got, ref)
 
 
-@pytest.mark.parametrize("name", ["bf16_B1_T65536_Hq16_Hkv2_d128_L24", "bf16_B1_T65536_Hq32_Hkv1_d128_L48"])
-def test_bwd_workload_T65536_sampled(name):
-    """At the 64K workloads: the query and depth-slot gradients of sampled
-    (b, t, kv head) groups against the oracle's per-group form, and the exact
-    sums (sum of dv over all keys = sum of dout; sum of dk = 0) per kv head."""
+@pytest.mark.parametrize("name", ["bf16_B2_T16384_Hq16_Hkv2_d128_L24", "bf16_B1_T65536_Hq16_Hkv2_d128_L24",
+                                  "bf16_B1_T65536_Hq32_Hkv1_d128_L48"])
+def test_bwd_workload_sampled(name):
+    """At the 16K and 64K workloads: the query and depth-slot gradients of
+    sampled (b, t, kv head) groups against the oracle's per-group form, and
+    the exact sums (sum of dv over all keys = sum of dout; sum of dk = 0) per
+    (batch, kv head)."""
     w = workload(name)
     _say(f"bwd {w['name']} (sampled groups + gradient sums)")
     B, T, Hq, Hkv, d, L_d = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
@@ -117,7 +119,8 @@ def test_bwd_workload_T65536_sampled(name):
     G = Hq // Hkv
     rng = np.random.default_rng(w["seed"] + 11)
     ts = sorted(set(rng.integers(0, T, 40).tolist()) | {0, 1, 63, 64, T // 2, T - 1})
-    groups = [(0, t, kvh) for t in ts for kvh in range(Hkv)]
+    groups = [(int(rng.integers(0, B)) if B > 1 else 0, t, kvh) for t in ts for kvh in range(Hkv)]
+    groups += [(B - 1, T - 1, kvh) for kvh in range(Hkv)] if B > 1 else []
     rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), groups=groups)
     gq = np.stack([dq[b, t, kvh * G:(kvh + 1) * G] for (b, t, kvh) in groups])
     gkd = np.stack([dkd[b, t, :, kvh] for (b, t, kvh) in groups])
@@ -126,14 +129,15 @@ def test_bwd_workload_T65536_sampled(name):
     errs = {"dq": _rel_err(gq, rq), "dk_depth": _rel_err(gkd, rkd), "dv_depth": _rel_err(gvd, rvd)}
     # exact sums, checked relative to the L1 size of the summands
     do = np32(dout).astype(np.float64)
-    for kvh in range(Hkv):
-        sv = dvs[0, :, kvh].sum(0) + dvd[0, :, :, kvh].sum((0, 1))
-        ref = do[0, :, kvh * G:(kvh + 1) * G].sum((0, 1))
-        l1v = np.abs(dvs[0, :, kvh]).sum(0) + np.abs(dvd[0, :, :, kvh]).sum((0, 1))
-        sk = dks[0, :, kvh].sum(0) + dkd[0, :, :, kvh].sum((0, 1))
-        l1k = np.abs(dks[0, :, kvh]).sum(0) + np.abs(dkd[0, :, :, kvh]).sum((0, 1))
-        errs[f"sum_dv[{kvh}]"] = float((np.abs(sv - ref) / l1v).max())
-        errs[f"sum_dk[{kvh}]"] = float((np.abs(sk) / l1k).max())
+    for b in range(B):
+        for kvh in range(Hkv):
+            sv = dvs[b, :, kvh].sum(0) + dvd[b, :, :, kvh].sum((0, 1))
+            ref = do[b, :, kvh * G:(kvh + 1) * G].sum((0, 1))
+            l1v = np.abs(dvs[b, :, kvh]).sum(0) + np.abs(dvd[b, :, :, kvh]).sum((0, 1))
+            sk = dks[b, :, kvh].sum(0) + dkd[b, :, :, kvh].sum((0, 1))
+            l1k = np.abs(dks[b, :, kvh]).sum(0) + np.abs(dkd[b, :, :, kvh]).sum((0, 1))
+            errs[f"sum_dv[{b},{kvh}]"] = float((np.abs(sv - ref) / l1v).max())
+            errs[f"sum_dk[{b},{kvh}]"] = float((np.abs(sk) / l1k).max())
     _say(f"{w['name']}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
     for k, v in errs.items():
         assert v <= tol, f"{k} error {v} > {tol}"
