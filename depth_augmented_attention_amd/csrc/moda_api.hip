@@ -71,8 +71,10 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   const bool fast = sizeof(E) == 2 && D == 128 && (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL &&
                     (long long)p.T * p.G * 4 < 0x7fffffffLL;
   if constexpr (sizeof(E) == 2 && D == 128) {
-    if (fast)
-      hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+    if (fast && 64 % p.G == 0)
+      hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, true>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+    else if (fast)
+      hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, false>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
     else
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
   } else {

@@ -657,7 +657,10 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
 //   * Q and dO blocks of 64 rows, with their lse and Delta, go from memory
 //     straight into LDS with the direct global->LDS loads (two stages, one
 //     barrier per block); rows of the GQA fold are gathered by per-lane
-//     offsets, rows past the end read as zeros.
+//     offsets, rows past the end read as zeros.  When G divides 64 (GP)
+//     every block starts at a whole position, so those offsets are lane
+//     constants and the block's position moves the buffer base; otherwise
+//     each block's offsets take a multiply-shift division by G.
 //   * One copy of each block serves both products: row-major reads for
 //     S = Q K^T and dP = dO V^T, and LDS transpose reads (ds_read_b64_tr_b16,
 //     through the compiler builtin; the two stages are separate arrays, so
@@ -696,7 +699,7 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, v
 
 }  // namespace bwdbf16
 
-template <int D>
+template <int D, bool GP>
 __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   static_assert(D == 128, "built for head size 128");
   using namespace bwdbf16;
@@ -767,26 +770,67 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rl2 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.work + p.BHT + lbase), (short)0, 0x7fffffff, kBufferWord3);  // -lse * sqrt(d)
 
+  // GP (G divides QB): every block starts at a whole position Rb / G, so row
+  // r of a block is position Rb / G + r / G, head r % G -- a lane-constant
+  // offset plus the block's position, which goes into the buffer base.
+  uint32_t qoff[LOADS], loff = 0;
+  if constexpr (GP) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = 4 * (i * NW + wave) + (lane >> 4);
+      const int lc = (lane & 15) ^ swz(r);
+      qoff[i] = (uint32_t)((((r / G) * Hq + r % G) * D + lc * 8) * 2);
+    }
+    const int r = wave * 64 + lane;             // lse / Delta row (waves < QB / 64)
+    loff = (uint32_t)(((r % G) * T + r / G) * 4);
+  }
+  const int log2g = p.g_shift - 31;             // log2 G when G is a power of two
+
   // block of rows [Rb, Rb + 64) -> stage st
   auto load_block = [&](int Rb, int st) {
     char* sb = st ? smem1 : smem0;
+    if constexpr (GP) {
+      const int lim = TG - Rb;                  // rows r < lim of the block exist
+      const long long tb = (long long)(Rb >> log2g);
+      const __amdgpu_buffer_rsrc_t bq = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const bf16*>(p.q) + qbase + tb * Hq * D), (short)0, 0x7fffffff, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t bo = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const bf16*>(p.dO) + qbase + tb * Hq * D), (short)0, 0x7fffffff, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int sp = i * NW + wave;             // 4-row span of the block
-      const int r = 4 * sp + (lane >> 4);
-      const int R = Rb + r;
-      const int t = div_g(R, p.g_magic, p.g_shift);
-      const int lc = (lane & 15) ^ swz(r);
-      const uint32_t off = R < TG ? (uint32_t)(((t * Hq + (R - t * G)) * D + lc * 8) * 2) : OOB;
-      dma16(rq, off, sb + sp * 1024);
-      dma16(ro, off, sb + OFF_O + sp * 1024);
-    }
-    if (wave < QB / 64) {
-      const int R = Rb + wave * 64 + lane;
-      const int t = div_g(R, p.g_magic, p.g_shift);
-      const uint32_t off = R < TG ? (uint32_t)(((R - t * G) * T + t) * 4) : OOB;
-      dma4(rl2, off, sb + OFF_L + wave * 256);
-      dma4(rd, off, sb + OFF_D + wave * 256);
+      for (int i = 0; i < LOADS; ++i) {
+        const int sp = i * NW + wave;
+        const uint32_t off = 4 * sp + (lane >> 4) < lim ? qoff[i] : OOB;
+        dma16(bq, off, sb + sp * 1024);
+        dma16(bo, off, sb + OFF_O + sp * 1024);
+      }
+      if (wave < QB / 64) {
+        const uint32_t off = wave * 64 + lane < lim ? loff : OOB;
+        const __amdgpu_buffer_rsrc_t bl = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.work + p.BHT + lbase + tb), (short)0, 0x7fffffff, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t bd = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.work + lbase + tb), (short)0, 0x7fffffff, kBufferWord3);
+        dma4(bl, off, sb + OFF_L + wave * 256);
+        dma4(bd, off, sb + OFF_D + wave * 256);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int sp = i * NW + wave;           // 4-row span of the block
+        const int r = 4 * sp + (lane >> 4);
+        const int R = Rb + r;
+        const int t = div_g(R, p.g_magic, p.g_shift);
+        const int lc = (lane & 15) ^ swz(r);
+        const uint32_t off = R < TG ? (uint32_t)(((t * Hq + (R - t * G)) * D + lc * 8) * 2) : OOB;
+        dma16(rq, off, sb + sp * 1024);
+        dma16(ro, off, sb + OFF_O + sp * 1024);
+      }
+      if (wave < QB / 64) {
+        const int R = Rb + wave * 64 + lane;
+        const int t = div_g(R, p.g_magic, p.g_shift);
+        const uint32_t off = R < TG ? (uint32_t)(((R - t * G) * T + t) * 4) : OOB;
+        dma4(rl2, off, sb + OFF_L + wave * 256);
+        dma4(rd, off, sb + OFF_D + wave * 256);
+      }
     }
   };
 
