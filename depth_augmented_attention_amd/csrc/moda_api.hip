@@ -62,11 +62,16 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   const long long rows = (long long)p.B * p.T * p.Hq;
   const long long rpb = 256 / (D / ve);
   hipLaunchKernelGGL((moda::moda_bwd_delta_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
+  // each launch is checked before the next, so that a failed launch is not
+  // hidden behind the ones after it
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const unsigned BH = (unsigned)(p.B * p.Hkv);
   if constexpr (sizeof(E) == 2 && D == 128)
     hipLaunchKernelGGL((moda::moda_bwd_dq_bf16_kernel<D>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
   else
     hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   // the bf16 d=128 kernel addresses one batch's q / dO and lse rows with 32-bit offsets
   const bool fast = sizeof(E) == 2 && D == 128 && (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL &&
                     (long long)p.T * p.G * 4 < 0x7fffffffLL;
@@ -80,6 +85,7 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
   }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.L_d > 0) {
     // whole positions per 32-row wave (G divides 32): the matrix-core depth kernel
     if (sizeof(E) == 2 && D == 128 && 32 % p.G == 0)
