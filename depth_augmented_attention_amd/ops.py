@@ -154,6 +154,8 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have the shape and dtype of q")
     if with_lse and lse is None:
         lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
     if lse is not None:
@@ -325,6 +327,8 @@ def moda_fwd_window_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have the shape and dtype of q")
     if with_lse and lse is None:
         lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
     if lse is not None:

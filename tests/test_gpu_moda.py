@@ -170,3 +170,9 @@ def test_errors_raise():
     k = torch.zeros(1, 4, 1, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(moda.ModaError):
         moda.moda_fwd(q, k, k, None, None, 0)          # d = 96 not built
+    q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):                    # caller's out too small
+        moda.moda_fwd(q, k, k, None, None, 0, out=torch.empty(1, 2, 2, 128, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):                    # caller's out of another dtype
+        moda.moda_fwd(q, k, k, None, None, 0, out=torch.empty(1, 4, 2, 128, dtype=torch.float32, device="cuda"))
