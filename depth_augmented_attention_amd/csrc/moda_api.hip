@@ -72,13 +72,15 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   else
     hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // the bf16 d=128 kernel addresses one batch's q / dO and lse rows with 32-bit offsets
-  const bool fast = sizeof(E) == 2 && D == 128 && (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL &&
-                    (long long)p.T * p.G * 4 < 0x7fffffffLL;
+  // the bf16 d=128 kernel addresses one kv head's lse rows with 32-bit
+  // offsets; with G not dividing 64 also one batch's q / dO rows (with G
+  // dividing 64 those offsets stay within one 64-row block)
+  const bool lse32 = (long long)p.T * p.G * 4 < 0x7fffffffLL;
+  const bool q32 = (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL;
   if constexpr (sizeof(E) == 2 && D == 128) {
-    if (fast && 64 % p.G == 0)
+    if (lse32 && 64 % p.G == 0)
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, true>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
-    else if (fast)
+    else if (lse32 && q32)
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, false>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
     else
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);

@@ -143,6 +143,45 @@ def test_bwd_workload_sampled(name):
         assert v <= tol, f"{k} error {v} > {tol}"
 
 
+def test_bwd_long_sequence():
+    """T * Hq * d * 2 bytes = 2^31 (past 32-bit byte offsets from the batch's
+    first row; G = 32 divides the 64-row blocks, so the dK/dV kernel addresses
+    rows from each block's base): sampled groups against the oracle and the
+    exact gradient sums."""
+    B, T, Hq, Hkv, d, L_d = 1, 262144, 32, 1, 128, 2
+    _say(f"bwd long sequence B{B} T{T} Hq{Hq} Hkv{Hkv} d{d} L{L_d}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype="bf16", seed=77)
+    dout = make_dout(B, T, Hq, d, dtype="bf16", seed=77)
+    dev = torch.device("cuda:0")
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    kp, vp = moda.moda_pack_depth(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd(qd, ksd, vsd, kp, vp, L_d)
+    dq, dks, dvs, dkd, dvd = moda.moda_bwd(qd, ksd, vsd, kp, vp, L_d, out, lse, dd)
+    torch.cuda.synchronize()
+    del out, lse, kp, vp
+    G = Hq // Hkv
+    rng = np.random.default_rng(78)
+    ts = sorted(set(rng.integers(0, T, 6).tolist()) | {0, 1, 63, 64, T // 2, T - 1})
+    groups = [(0, t, 0) for t in ts]
+    rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), groups=groups)
+    idx = torch.tensor(ts, device=dev)
+    gq = dq[0].index_select(0, idx).double().cpu().numpy()            # [n, Hq, d]
+    gkd = dkd[0].index_select(0, idx)[:, :, 0].double().cpu().numpy()  # [n, L_d, d]
+    gvd = dvd[0].index_select(0, idx)[:, :, 0].double().cpu().numpy()
+    errs = {"dq": _rel_err(gq, rq), "dk_depth": _rel_err(gkd, rkd), "dv_depth": _rel_err(gvd, rvd)}
+    dvs_, dks_ = dvs[0, :, 0].double().cpu().numpy(), dks[0, :, 0].double().cpu().numpy()
+    dvd_, dkd_ = dvd[0, :, :, 0].double().cpu().numpy(), dkd[0, :, :, 0].double().cpu().numpy()
+    ref = dout[0].sum((0, 1), dtype=torch.float64).numpy()
+    sv = dvs_.sum(0) + dvd_.sum((0, 1))
+    sk = dks_.sum(0) + dkd_.sum((0, 1))
+    errs["sum_dv"] = float((np.abs(sv - ref) / (np.abs(dvs_).sum(0) + np.abs(dvd_).sum((0, 1)))).max())
+    errs["sum_dk"] = float((np.abs(sk) / (np.abs(dks_).sum(0) + np.abs(dkd_).sum((0, 1)))).max())
+    tol = TOL_BWD[torch.bfloat16]
+    _say("long sequence: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{k} error {v} > {tol}"
+
+
 @pytest.mark.parametrize("case", [("bf16", 1, 180, 8, 2, 128, 6, 2, 5), ("fp32", 1, 70, 4, 1, 64, 5, 3, 5),
                                   ("bf16", 1, 100, 6, 2, 128, 4, 0, 4)])
 def test_bwd_window_parity(case):
