@@ -29,6 +29,7 @@ METRIC = "MoDA fwd TFLOP/s (bf16, T=64K) + % MFMA peak; overhead vs L_d=0"
 DEFAULT_WORKLOAD = "bf16_B1_T65536_Hq16_Hkv2_d128_L24"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 512 << 20                             # > L2 + the 256 MB MALL
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -233,18 +234,30 @@ def main():
     res["pack_gbps"] = 2 * 2 * kd.numel() * kd.element_size() / (avg_pack * 1e-3) / 1e9
     res["fwd_compulsory_gbps"] = compulsory_bytes(w) / (avg_fwd * 1e-3) / 1e9
 
+    # Cache flush: a 512 MiB fill before each launch timed on its own, so that
+    # neither L2 nor the 256 MB MALL still holds that launch's inputs (in the
+    # timed steps above the depth repack, which streams 3.2 GB, does this).
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    res["cache_flush_bytes"] = FLUSH_BYTES
+
+    def timed_launches(fn, reps):
+        """Per-launch times (ms) of fn(), each after a cache flush; HIP events
+        on the current stream around the launch only."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            flush_buf.fill_(i & 0xFF)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
     if not args.no_l0 and L_d > 0:
         log("timing the same kernel at L_d = 0")
         for _ in range(2):
             moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
         torch.cuda.synchronize()
-        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        e0[0].record()
-        for i in range(args.steps):
-            moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
-            e0[i + 1].record()
-        torch.cuda.synchronize()
-        l0 = [e0[i].elapsed_time(e0[i + 1]) for i in range(args.steps)]
+        l0 = timed_launches(lambda: moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse), args.steps)
         avg_l0 = sum(l0) / len(l0)
         res["fwd_ms_L0"] = avg_l0
         res["fwd_tflops_L0"] = useful_flops(B, T, Hq, d, 0) / (avg_l0 * 1e-3) / 1e12
@@ -343,14 +356,8 @@ def main():
             def timed(Ld, kp_, vp_):
                 moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl)
                 torch.cuda.synchronize()
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-                e[0].record()
-                for i in range(reps):
-                    moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl)
-                    e[i + 1].record()
-                torch.cuda.synchronize()
-                ts = sorted(e[i].elapsed_time(e[i + 1]) for i in range(reps))
-                return ts[len(ts) // 2]                       # median
+                ts = sorted(timed_launches(lambda: moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl), reps))
+                return ts[len(ts) // 2]                       # median, each launch after a cache flush
 
             t_d = timed(sL, skp, svp)
             t_0 = timed(0, None, None)
