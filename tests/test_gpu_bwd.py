@@ -74,6 +74,12 @@ CASES = [
     ("bf16_T200_G4_d128_L0", "bf16", 1, 200, 4, 1, 128, 0),
     ("bf16_T1_G2_d128_L3", "bf16", 1, 1, 4, 2, 128, 3),
     ("bf16_T257_G8_d128_L40", "bf16", 1, 257, 16, 2, 128, 40),
+    # G dividing 64 (dK/dV rows addressed from each block's base) and not
+    ("bf16_B2_T150_G1_d128_L3", "bf16", 2, 150, 2, 2, 128, 3),
+    ("bf16_T100_G64_d128_L2", "bf16", 1, 100, 64, 1, 128, 2),
+    ("bf16_T70_G16_d128_L5", "bf16", 1, 70, 32, 2, 128, 5),
+    ("bf16_T90_G12_d128_L3", "bf16", 1, 90, 12, 1, 128, 3),
+    ("bf16_T33_G5_d128_L0", "bf16", 1, 33, 5, 1, 128, 0),
 ]
 
 
