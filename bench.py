@@ -331,6 +331,21 @@ def main():
         res["q8_fwd_tflops"] = F / (q8_fwd_ms * 1e-3) / 1e12
         if "fwd_ms_L0" in res:
             res["q8_overhead_vs_L0"] = q8_fwd_ms / res["fwd_ms_L0"] - 1.0
+        if not args.no_bwd:
+            # backward over the 8-bit depth KV (mean of 2 calls after one warm-up)
+            from moda_inputs import make_dout
+            dq8 = make_dout(B, T, Hq, d, dtype=w["dtype"], seed=w["seed"]).to(q.device)
+            moda.moda_fwd_q8(q, ks, vs, packed, L_d, out=out, lse=lse)
+            g8 = moda.moda_bwd_q8(q, ks, vs, packed, L_d, out, lse, dq8)
+            torch.cuda.synchronize()
+            e8 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e8[0].record()
+            for i in range(2):
+                moda.moda_bwd_q8(q, ks, vs, packed, L_d, out, lse, dq8, grads=g8)
+                e8[i + 1].record()
+            torch.cuda.synchronize()
+            res["q8_bwd_ms"] = e8[0].elapsed_time(e8[2]) / 2
+            del g8, dq8
         del packed
 
     if not args.no_sweep:

@@ -20,7 +20,8 @@ MODA_ERR_HIP = 5
 # every symbol include/moda.h declares
 EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
            "moda_append_depth", "moda_bwd", "moda_bwd_window", "moda_pack_depth_q8", "moda_fwd_q8",
-           "moda_fwd_window_q8", "moda_append_depth_q8", "moda_status_string")
+           "moda_fwd_window_q8", "moda_append_depth_q8", "moda_bwd_q8", "moda_bwd_window_q8",
+           "moda_status_string")
 
 
 class ModaError(RuntimeError):
@@ -65,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.moda_fwd_window_q8.restype = c_int
     lib.moda_append_depth_q8.argtypes = [c_vp] * 6 + [c_int] * 7 + [c_vp]
     lib.moda_append_depth_q8.restype = c_int
+    lib.moda_bwd_q8.argtypes = [c_vp] * 16 + [c_int] * 7 + [c_vp]
+    lib.moda_bwd_q8.restype = c_int
+    lib.moda_bwd_window_q8.argtypes = [c_vp] * 16 + [c_int] * 9 + [c_vp]
+    lib.moda_bwd_window_q8.restype = c_int
     lib.moda_status_string.argtypes = [c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -289,7 +289,8 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
 }
 
 static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
-                    const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+                    const void* v_depth, const float* k_scale, const float* v_scale, int q8,
+                    const void* out, const float* lse, const void* dout, void* dq,
                     void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
                     int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
                     void* stream) {
@@ -303,6 +304,7 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
     return MODA_ERR_NULL;
   const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
+  if (L_d > 0 && q8 && (!k_scale || !v_scale)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
   const long long ntiles = (rows + 32 * kWaves - 1) / (32 * kWaves);
@@ -314,6 +316,7 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
 
   moda::BwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
+  p.ksc = k_scale; p.vsc = v_scale; p.q8 = q8;
   p.o = out; p.dO = dout; p.lse = lse; p.work = work; p.BHT = (long long)B * Hq * T;
   p.dq = dq; p.dk = dk_seq; p.dv = dv_seq; p.dkd = dk_depth; p.dvd = dv_depth;
   p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
@@ -345,8 +348,8 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
              void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B, int T,
              int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
   if (L_d < 0) return MODA_ERR_SHAPE;
-  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, dq, dk_seq, dv_seq, dk_depth,
-                  dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
+                  dv_seq, dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
 }
 
 int moda_bwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
@@ -354,8 +357,27 @@ int moda_bwd_window(const void* q, const void* k_seq, const void* v_seq, const v
                     void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
                     int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
                     void* stream) {
-  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, out, lse, dout, dq, dk_seq, dv_seq, dk_depth,
-                  dv_depth, work, B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, dtype, stream);
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
+                  dv_seq, dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, dtype,
+                  stream);
+}
+
+int moda_bwd_q8(const void* q, const void* k_seq, const void* v_seq, const int8_t* k_q, const int8_t* v_q,
+                const float* k_scale, const float* v_scale, const void* out, const float* lse,
+                const void* dout, void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+                float* work, int B, int T, int Hq, int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return bwd_impl(q, k_seq, v_seq, k_q, v_q, k_scale, v_scale, 1, out, lse, dout, dq, dk_seq, dv_seq,
+                  dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
+}
+
+int moda_bwd_window_q8(const void* q, const void* k_seq, const void* v_seq, const int8_t* k_q,
+                       const int8_t* v_q, const float* k_scale, const float* v_scale, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk_seq, void* dv_seq,
+                       void* dk_depth, void* dv_depth, float* work, int B, int T, int Hq, int Hkv, int d,
+                       int L_cap, int slot_lo, int slot_hi, int dtype, void* stream) {
+  return bwd_impl(q, k_seq, v_seq, k_q, v_q, k_scale, v_scale, 1, out, lse, dout, dq, dk_seq, dv_seq,
+                  dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, dtype, stream);
 }
 
 }  // extern "C"

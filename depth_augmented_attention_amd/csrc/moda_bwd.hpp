@@ -46,8 +46,11 @@ struct BwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* kd;      // packed depth keys   [B][Hkv][NKp][D]
+  const void* kd;      // packed depth keys   [B][Hkv][NKp][D] (dtype, or int8 codes when q8)
   const void* vd;      // packed depth values [B][Hkv][NKp][D]
+  const float* ksc;    // q8: float32 scale per packed key row   [B][Hkv][NKp]
+  const float* vsc;    // q8: float32 scale per packed value row [B][Hkv][NKp]
+  int q8;              // depth KV stored as int8 codes + row scales
   const void* o;       // forward output [B,T,Hq,D]
   const void* dO;      // gradient of the output [B,T,Hq,D]
   const float* lse;    // forward lse [B,Hq,T] (natural log)
@@ -153,15 +156,30 @@ __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw
   const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
   const E* kdb = reinterpret_cast<const E*>(p.kd) + (long long)bh * p.NKp * D;
   const E* vdb = reinterpret_cast<const E*>(p.vd) + (long long)bh * p.NKp * D;
+  // 8-bit depth KV: codes and row scales of this (b, kv head)
+  const int8_t* kq8 = reinterpret_cast<const int8_t*>(p.kd) + (long long)bh * p.NKp * D;
+  const int8_t* vq8 = reinterpret_cast<const int8_t*>(p.vd) + (long long)bh * p.NKp * D;
+  const float* ks8 = p.q8 ? p.ksc + (long long)bh * p.NKp : nullptr;
+  const float* vs8 = p.q8 ? p.vsc + (long long)bh * p.NKp : nullptr;
   for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
     if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
     f32x16 s = f32x16{}, dp = f32x16{};
-    const E* krow = kdb + (n0 + key_row) * D + hh * 8;
-    const E* vrow = vdb + (n0 + key_row) * D + hh * 8;
+    if (p.q8) {
+      const long long kr = n0 + key_row;
+      const float ks = ks8[kr], vs = vs8[kr];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      s = mma16(load_frag(krow + kc * 16), qf[kc], s);
-      dp = mma16(load_frag(vrow + kc * 16), df[kc], dp);
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mma16(Dequant<E>::frag(kq8 + kr * D + hh * 8 + kc * 16, ks), qf[kc], s);
+        dp = mma16(Dequant<E>::frag(vq8 + kr * D + hh * 8 + kc * 16, vs), df[kc], dp);
+      }
+    } else {
+      const E* krow = kdb + (n0 + key_row) * D + hh * 8;
+      const E* vrow = vdb + (n0 + key_row) * D + hh * 8;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mma16(load_frag(krow + kc * 16), qf[kc], s);
+        dp = mma16(load_frag(vrow + kc * 16), df[kc], dp);
+      }
     }
     const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
     const long long own_hi = own_lo + L_d;
@@ -180,7 +198,10 @@ __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw
       for (int dt = 0; dt < NDT; ++dt) {
         Frag kt;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kt[j] = kdb[(n0 + c * 16 + hh * 8 + j) * D + dt * 32 + n];
+        for (int j = 0; j < 8; ++j) {
+          const long long r = n0 + c * 16 + hh * 8 + j;
+          kt[j] = p.q8 ? Dequant<E>::one(kq8[r * D + dt * 32 + n], ks8[r]) : kdb[r * D + dt * 32 + n];
+        }
         acc[dt] = mma16(kt, f, acc[dt]);
       }
     }
@@ -562,6 +583,10 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
   const long long bh = (long long)b * Hkv + kvh;
   const E* kdb = reinterpret_cast<const E*>(p.kd) + bh * p.NKp * D;
   const E* vdb = reinterpret_cast<const E*>(p.vd) + bh * p.NKp * D;
+  const int8_t* kq8 = reinterpret_cast<const int8_t*>(p.kd) + bh * p.NKp * D;   // q8 codes
+  const int8_t* vq8 = reinterpret_cast<const int8_t*>(p.vd) + bh * p.NKp * D;
+  const float* ks8 = p.q8 ? p.ksc + bh * p.NKp : nullptr;                      // q8 row scales
+  const float* vs8 = p.q8 ? p.vsc + bh * p.NKp : nullptr;
   const E* qg = reinterpret_cast<const E*>(p.q);
   const E* og = reinterpret_cast<const E*>(p.dO);
   const float scale = p.scale;
@@ -573,14 +598,20 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_kernel(BwdParams p) {
     for (int i = tid; i < LC * D; i += 256) {
       const int j = i / D, e = i % D;
       float kv = 0.f;
-      if (j < nj) kv = (float)kdb[((long long)t * p.L_cap + p.slot_lo + j0 + j) * D + e];
+      if (j < nj) {
+        const long long r = (long long)t * p.L_cap + p.slot_lo + j0 + j;
+        kv = p.q8 ? (float)Dequant<E>::one(kq8[r * D + e], ks8[r]) : (float)kdb[r * D + e];
+      }
       sk[j * LDF + e] = kv;
     }
     // values: rows of the packed values, dims fastest
     for (int i = tid; i < LC * D; i += 256) {
       const int j = i / D, e = i % D;
       float vv = 0.f;
-      if (j < nj) vv = (float)vdb[((long long)t * p.L_cap + p.slot_lo + j0 + j) * D + e];
+      if (j < nj) {
+        const long long r = (long long)t * p.L_cap + p.slot_lo + j0 + j;
+        vv = p.q8 ? (float)Dequant<E>::one(vq8[r * D + e], vs8[r]) : (float)vdb[r * D + e];
+      }
       sv[j * LDF + e] = vv;
     }
     float accK[EPT], accV[EPT];
@@ -1251,10 +1282,22 @@ __global__ __launch_bounds__(256) void moda_bwd_depth_bf16_kernel(BwdParams p) {
     const bool key_ok = tk < T && slot >= 0 && slot < L_d;
     const int r_lo = tk * G;                      // rows [r_lo, r_lo + G) sit at position tk
     bf16x8 kf[NKC], vf[NKC];
+    if (p.q8) {
+      const long long r = (long long)bh * p.NKp + key;
+      const int8_t* kq = reinterpret_cast<const int8_t*>(p.kd) + r * D + hh * 8;
+      const int8_t* vq = reinterpret_cast<const int8_t*>(p.vd) + r * D + hh * 8;
+      const float ks = p.ksc[r], vs = p.vsc[r];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      kf[kc] = load_frag(kdb + key * D + kc * 16 + hh * 8);
-      vf[kc] = load_frag(vdb + key * D + kc * 16 + hh * 8);
+      for (int kc = 0; kc < NKC; ++kc) {
+        kf[kc] = dequant_frag_bf16(kq + kc * 16, ks);
+        vf[kc] = dequant_frag_bf16(vq + kc * 16, vs);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        kf[kc] = load_frag(kdb + key * D + kc * 16 + hh * 8);
+        vf[kc] = load_frag(vdb + key * D + kc * 16 + hh * 8);
+      }
     }
     f32x16 s, dp;
 #pragma unroll

@@ -189,14 +189,9 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                            grads=grads, work=work, stream=stream)
 
 
-def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
-                    k_depth: torch.Tensor | None, v_depth: torch.Tensor | None,
-                    L_cap: int, slot_lo: int, slot_hi: int,
-                    out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
-                    grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
-    """Gradients of moda_fwd_window(..., L_cap, slot_lo, slot_hi): as
-    moda_bwd, with the depth gradients of slots slot_lo .. slot_hi-1
-    ([B,T,slot_hi-slot_lo,Hkv,d])."""
+def _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout, grads, work):
+    """Shape / dtype / device checks shared by the backward calls; allocates
+    the gradients and the work buffer when not given."""
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
     B, T, Hq, d = q.shape
@@ -214,16 +209,6 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                     (dout, "dout")):
         _dev(t, name)
     L_d = slot_hi - slot_lo
-    kd_ptr = vd_ptr = None
-    if L_d > 0:
-        if k_depth is None or v_depth is None:
-            raise ValueError("packed depth buffers are required when slots are read")
-        n = depth_packed_elems(B, T, Hkv, d, L_cap)
-        for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
-            _dev(t, name)
-            if t.numel() != n or t.dtype != q.dtype:
-                raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
-        kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
     Ld = max(L_d, 0)
     shapes = [(B, T, Hq, d), (B, T, Hkv, d), (B, T, Hkv, d), (B, T, Ld, Hkv, d), (B, T, Ld, Hkv, d)]
     if grads is None:
@@ -241,6 +226,29 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     _dev(work, "work")
     if work.dtype != torch.float32 or work.shape != (2, B, Hq, T):
         raise ValueError("work must be float32 [2,B,Hq,T]")
+    return (B, T, Hq, Hkv, d, L_d), grads, work
+
+
+def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+                    k_depth: torch.Tensor | None, v_depth: torch.Tensor | None,
+                    L_cap: int, slot_lo: int, slot_hi: int,
+                    out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                    grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
+    """Gradients of moda_fwd_window(..., L_cap, slot_lo, slot_hi): as
+    moda_bwd, with the depth gradients of slots slot_lo .. slot_hi-1
+    ([B,T,slot_hi-slot_lo,Hkv,d])."""
+    (B, T, Hq, Hkv, d, L_d), grads, work = _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout,
+                                                       grads, work)
+    kd_ptr = vd_ptr = None
+    if L_d > 0:
+        if k_depth is None or v_depth is None:
+            raise ValueError("packed depth buffers are required when slots are read")
+        n = depth_packed_elems(B, T, Hkv, d, L_cap)
+        for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+            _dev(t, name)
+            if t.numel() != n or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
+        kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
     ptr = [g.data_ptr() if g is not None else None for g in grads]
     dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
                       dout, work, *grads[:3], *(grads[3:] if L_d > 0 else ()))
@@ -251,6 +259,37 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
         _dtype_code(q))
     check(st, "moda_bwd_window")
     return grads
+
+
+def moda_bwd_window_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8,
+                       L_cap: int, slot_lo: int, slot_hi: int,
+                       out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                       grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
+    """Gradients of moda_fwd_window_q8(..., L_cap, slot_lo, slot_hi): as
+    moda_bwd_window, the depth keys and values read from the four 8-bit
+    buffers of moda_pack_depth_q8 / moda_append_depth_q8; the depth
+    gradients are those of the dequantised keys and values."""
+    (B, T, Hq, Hkv, d, L_d), grads, work = _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout,
+                                                       grads, work)
+    ptrs = _check_q8(packed_q8, B, T, Hkv, d, L_cap) if L_d > 0 else [None] * 4
+    ptr = [g.data_ptr() if g is not None else None for g in grads]
+    dev = _one_device(q, k_seq, v_seq, *(packed_q8 if L_d > 0 else ()), out, lse, dout, work, *grads[:3],
+                      *(grads[3:] if L_d > 0 else ()))
+    st = _call(dev, "moda_bwd_window_q8", stream,
+        q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), *ptrs,
+        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+        ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi,
+        _dtype_code(q))
+    check(st, "moda_bwd_window_q8")
+    return grads
+
+
+def moda_bwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packed_q8, L_d: int,
+                out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
+    """Gradients of moda_fwd_q8 (the four buffers of moda_pack_depth_q8)."""
+    return moda_bwd_window_q8(q, k_seq, v_seq, packed_q8, L_d, 0, L_d, out, lse, dout,
+                              grads=grads, work=work, stream=stream)
 
 
 def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None):

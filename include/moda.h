@@ -284,6 +284,40 @@ int moda_append_depth_q8(const void* k_new, const void* v_new,
                          int B, int T, int Hkv, int d, int L_cap, int slot, int dtype,
                          void* stream);
 
+/*
+ * moda_bwd_q8 -- moda_bwd for moda_fwd_q8: the depth keys and values are read
+ * as int8 codes and float32 row scales (moda_pack_depth_q8) and dequantised
+ * (scale * code, rounded to dtype) as in the forward; dk_depth / dv_depth are
+ * the gradients with respect to those dequantised keys and values (the
+ * quantisation itself is not differentiated), in the logical layout of
+ * moda_bwd.  mhpn.cn article, section 4.2 (8-bit depth KV) for the storage;
+ * the derivatives as for moda_bwd.  Other arguments and errors as for
+ * moda_bwd; k_scale / v_scale NULL iff L_d == 0.
+ */
+int moda_bwd_q8(const void* q, const void* k_seq, const void* v_seq,
+                const int8_t* k_q, const int8_t* v_q,
+                const float* k_scale, const float* v_scale,
+                const void* out, const float* lse, const void* dout,
+                void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+                float* work,
+                int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+                void* stream);
+
+/*
+ * moda_bwd_window_q8 -- moda_bwd_window over 8-bit depth KV (the buffers of
+ * moda_fwd_window_q8 with L_cap slots per position): gradients of slots
+ * slot_lo .. slot_hi-1, logical [B, T, slot_hi - slot_lo, Hkv, d].
+ */
+int moda_bwd_window_q8(const void* q, const void* k_seq, const void* v_seq,
+                       const int8_t* k_q, const int8_t* v_q,
+                       const float* k_scale, const float* v_scale,
+                       const void* out, const float* lse, const void* dout,
+                       void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+                       float* work,
+                       int B, int T, int Hq, int Hkv, int d,
+                       int L_cap, int slot_lo, int slot_hi, int dtype,
+                       void* stream);
+
 /* Static, human-readable name of a moda_status value. */
 const char* moda_status_string(int status);
 

@@ -54,6 +54,13 @@ int main(void) {
                          2, MODA_BF16, NULL),
          MODA_ERR_SHAPE);
 
+  EXPECT(moda_bwd_q8(F, F, F, (int8_t*)F, (int8_t*)F, NULL, (float*)F, F, (const float*)F, F, F, F, F, F, F,
+                     (float*)F, 1, 4, 2, 1, 128, 3, MODA_BF16, NULL),
+         MODA_ERR_NULL);
+  EXPECT(moda_bwd_window_q8(F, F, F, (int8_t*)F, (int8_t*)F, (float*)F, (float*)F, F, (const float*)F, F, F, F,
+                            F, F, F, (float*)F, 1, 4, 2, 1, 128, 4, 3, 2, MODA_BF16, NULL),
+         MODA_ERR_SHAPE);
+
   EXPECT(strcmp(moda_status_string(MODA_OK), "MODA_OK"), 0);
   EXPECT(strncmp(moda_status_string(MODA_ERR_NULL), "MODA_ERR_NULL", 13), 0);
 

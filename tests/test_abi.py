@@ -178,6 +178,21 @@ def test_window_q8_and_bwd_window_validation():
     assert lib.moda_bwd_window(*ptrs, 1, 4, 2, 1, 128, 4, 1, 3, 1, None) == _lib.MODA_ERR_NULL
 
 
+def test_bwd_q8_validation():
+    lib = moda.load()
+    # q k v kq vq ks vs out lse dout dq dk dv dkd dvd work
+    ok = [FAKE] * 16
+    for i in (5, 6):                               # a NULL row scale with slots read
+        ptrs = list(ok)
+        ptrs[i] = None
+        assert lib.moda_bwd_q8(*ptrs, 1, 4, 2, 1, 128, 3, 1, None) == _lib.MODA_ERR_NULL
+    assert lib.moda_bwd_q8(*ok, 1, 4, 2, 1, 128, -1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_bwd_q8(*ok, 1, 4, 2, 1, 96, 3, 1, None) == _lib.MODA_ERR_UNSUPPORTED
+    assert lib.moda_bwd_window_q8(*ok, 1, 4, 2, 1, 128, 4, 3, 2, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_bwd_window_q8(*ok, 1, 4, 2, 1, 128, 4, 0, 5, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_bwd_window_q8(*ok, 1, 1 << 20, 2, 1, 128, 1 << 11, 0, 1, 1, None) == _lib.MODA_ERR_SHAPE
+
+
 def test_packed_key_index_bound():
     # T * L_cap must leave the packed key index n = t * L_cap + slot (plus the
     # padding to 32) inside 31 bits: every entry point that takes a depth

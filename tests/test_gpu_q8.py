@@ -1,6 +1,7 @@
 """GPU parity of 8-bit depth KV: moda_pack_depth_q8 codes and scales bit for
-bit against the oracle's quantisation, and moda_fwd_q8 against the forward
-oracle on the dequantised depth KV."""
+bit against the oracle's quantisation, moda_fwd_q8 against the forward oracle
+on the dequantised depth KV, and moda_bwd_q8 against the backward oracle on
+the same dequantised depth KV."""
 from __future__ import annotations
 
 import numpy as np
@@ -9,8 +10,8 @@ import torch
 
 import depth_augmented_attention_amd as moda
 from moda_check import TOL, np32
-from moda_inputs import make_inputs, sample_rows, workload
-from oracle import moda_forward
+from moda_inputs import make_dout, make_inputs, sample_rows, workload
+from oracle import moda_backward, moda_forward
 from oracle.moda_quant import dequantize_rows, quantize_rows
 
 pytestmark = pytest.mark.gpu
@@ -194,3 +195,53 @@ def test_fwd_window_q8_parity(case):
     ref_out, ref_lse = moda_forward(np32(q), np32(ks), np32(vs), _deq_logical(kd)[:, :, lo:hi],
                                     _deq_logical(vd)[:, :, lo:hi])
     _check(f"window q8 {case}", q.dtype, out, lse, ref_out, ref_lse)
+
+
+# max |gpu - oracle| / max(1, max |oracle|) per gradient (as for moda_bwd)
+TOL_BWD = {torch.float32: 1e-5, torch.bfloat16: 1.5e-2}
+BWD_CASES = [
+    # dtype, B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi
+    ("bf16", 1, 200, 16, 2, 128, 5, 0, 5),    # matrix-core depth kernel (G = 8)
+    ("bf16", 2, 97, 6, 2, 128, 4, 0, 4),      # G = 3: vector-unit depth kernel
+    ("fp32", 1, 90, 4, 1, 64, 3, 0, 3),       # generic kernels throughout
+    ("bf16", 1, 150, 8, 2, 128, 6, 2, 5),     # a window of the slots
+    ("fp32", 1, 70, 6, 2, 128, 5, 1, 4),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[
+    f"{c[0]}_B{c[1]}_T{c[2]}_Hq{c[3]}_Hkv{c[4]}_d{c[5]}_cap{c[6]}_{c[7]}-{c[8]}" for c in BWD_CASES])
+def test_bwd_q8_parity(case):
+    dtype, B, T, Hq, Hkv, d, L_cap, lo, hi = case
+    _say(f"bwd q8 {case}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_cap, dtype=dtype, seed=110 + T)
+    kd, vd = _with_zero_rows(kd, vd)
+    dout = make_dout(B, T, Hq, d, dtype=dtype, seed=110 + T)
+    dev = torch.device("cuda:0")
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    packed = moda.moda_pack_depth_q8(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd_window_q8(qd, ksd, vsd, packed, L_cap, lo, hi)
+    grads = moda.moda_bwd_window_q8(qd, ksd, vsd, packed, L_cap, lo, hi, out, lse, dd)
+    torch.cuda.synchronize()
+    refs = moda_backward(np32(q), np32(ks), np32(vs), _deq_logical(kd)[:, :, lo:hi],
+                         _deq_logical(vd)[:, :, lo:hi], np32(dout))
+    tol = TOL_BWD[q.dtype]
+    for nm, g, r in zip(("dq", "dk_seq", "dv_seq", "dk_depth", "dv_depth"), grads, refs):
+        e = float(np.abs(g.double().cpu().numpy() - r).max()) / max(1.0, float(np.abs(r).max()))
+        _say(f"  {nm}: {e:.2e}  (tol {tol:g})")
+        assert e <= tol, f"{case}: {nm} error {e} > {tol}"
+
+
+def test_bwd_q8_full_window_is_bwd_q8():
+    # moda_bwd_q8(..., L_d) is moda_bwd_window_q8(..., L_cap = L_d, 0, L_d): same bits
+    q, ks, vs, kd, vd = make_inputs(1, 120, 8, 2, 128, 4, dtype="bf16", seed=5)
+    dout = make_dout(1, 120, 8, 128, dtype="bf16", seed=5)
+    dev = torch.device("cuda:0")
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    packed = moda.moda_pack_depth_q8(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd_q8(qd, ksd, vsd, packed, 4)
+    a = moda.moda_bwd_q8(qd, ksd, vsd, packed, 4, out, lse, dd)
+    b = moda.moda_bwd_window_q8(qd, ksd, vsd, packed, 4, 0, 4, out, lse, dd)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -1,6 +1,6 @@
 """GPU parity on seeded random shapes: the forward over a random depth-slot
 window (bf16 or 8-bit depth KV), and for some shapes the backward of that
-window, each against the oracle.
+window (over the same depth KV), each against the oracle.
 
 The shapes are drawn once from a fixed seed (the list is the same on every
 run): dtype, head size, kv heads, GQA group size, batch, sequence length
@@ -39,7 +39,7 @@ def _draw_cases(n=28, seed=2026):
         lo = int(rng.integers(0, L_cap + 1))
         hi = int(rng.integers(lo, L_cap + 1))
         q8 = bool(rng.integers(0, 3) == 0) and hi > lo
-        bwd = bool(rng.integers(0, 3) == 0) and not q8
+        bwd = bool(rng.integers(0, 3) == 0)
         cases.append((f"r{i:02d}", dtype, B, T, G * Hkv, Hkv, d, L_cap, lo, hi, q8, bwd))
     return cases
 
@@ -85,7 +85,10 @@ def test_random_shape(case):
     if not bwd:
         return
     dout = make_dout(B, T, Hq, d, dtype=dtype, seed=500 + int(name[1:]))
-    grads = moda.moda_bwd_window(qd, ksd, vsd, kp, vp, L_cap, lo, hi, out, lse, dout.to(dev))
+    if q8:
+        grads = moda.moda_bwd_window_q8(qd, ksd, vsd, packed, L_cap, lo, hi, out, lse, dout.to(dev))
+    else:
+        grads = moda.moda_bwd_window(qd, ksd, vsd, kp, vp, L_cap, lo, hi, out, lse, dout.to(dev))
     torch.cuda.synchronize()
     refs = moda_backward(np32(q), np32(ks), np32(vs), kref, vref, np32(dout))
     tol = TOL_BWD[q.dtype]
