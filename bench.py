@@ -240,36 +240,45 @@ def main():
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     res["cache_flush_bytes"] = FLUSH_BYTES
 
-    def timed_launches(fn, reps):
-        """Per-launch times (ms) of fn(), each after a cache flush; HIP events
-        on the current stream around the launch only."""
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    def timed_launches(fns, reps):
+        """Per-launch times (ms) of each function in fns, the functions taken
+        in turn (so that both see the same clock and temperature), each launch
+        after a cache flush; HIP events on the current stream around the
+        launch only."""
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+              for _ in fns]
         for i in range(reps):
-            flush_buf.fill_(i & 0xFF)
-            ev[i][0].record()
-            fn()
-            ev[i][1].record()
+            for f, fn in enumerate(fns):
+                flush_buf.fill_(i & 0xFF)
+                ev[f][i][0].record()
+                fn()
+                ev[f][i][1].record()
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in ev]
+        return [[a.elapsed_time(b) for a, b in e] for e in ev]
 
     if not args.no_l0 and L_d > 0:
         log("timing the same kernel at L_d = 0")
         for _ in range(2):
             moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
         torch.cuda.synchronize()
-        l0 = timed_launches(lambda: moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse), args.steps)
+        # the same kernel with and without the depth slots, alternating, each
+        # launch after the cache fill
+        ld, l0 = timed_launches([lambda: moda.moda_fwd(q, ks, vs, kp, vp, L_d, out=out, lse=lse),
+                                 lambda: moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)], args.steps)
         avg_l0 = sum(l0) / len(l0)
+        avg_ld = sum(ld) / len(ld)
         res["fwd_ms_L0"] = avg_l0
+        res["fwd_ms_flushed"] = avg_ld
         res["fwd_tflops_L0"] = useful_flops(B, T, Hq, d, 0) / (avg_l0 * 1e-3) / 1e12
-        res["overhead_vs_L0"] = avg_fwd / avg_l0 - 1.0
-        res["overhead_vs_L0_with_pack"] = (avg_fwd + avg_pack) / avg_l0 - 1.0
+        res["overhead_vs_L0"] = avg_ld / avg_l0 - 1.0
+        res["overhead_vs_L0_with_pack"] = (avg_ld + avg_pack) / avg_l0 - 1.0
         # depth stream: its bytes over the time the depth slots add to the
         # forward (above the HBM peak means the stream is hidden under the sweep)
         depth_stream_bytes = 2.0 * B * T * L_d * Hkv * d * q.element_size()
         res["depth_stream_bytes"] = depth_stream_bytes
-        res["depth_incremental_ms"] = avg_fwd - avg_l0
-        res["depth_stream_gbps_incremental"] = (depth_stream_bytes / ((avg_fwd - avg_l0) * 1e-3) / 1e9
-                                                if avg_fwd > avg_l0 else None)
+        res["depth_incremental_ms"] = avg_ld - avg_l0
+        res["depth_stream_gbps_incremental"] = (depth_stream_bytes / ((avg_ld - avg_l0) * 1e-3) / 1e9
+                                                if avg_ld > avg_l0 else None)
         log(f"L_d=0 fwd {avg_l0:.3f} ms, overhead {100 * res['overhead_vs_L0']:.2f}%")
 
     if not args.no_extras and L_d > 0:
@@ -368,14 +377,13 @@ def main():
             sl = torch.empty(sB, sHq, sT, dtype=torch.float32, device=dev)
             reps = 20 if sT <= 16384 else 5
 
-            def timed(Ld, kp_, vp_):
-                moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl)
-                torch.cuda.synchronize()
-                ts = sorted(timed_launches(lambda: moda.moda_fwd(sq, sk, sv, kp_, vp_, Ld, out=so, lse=sl), reps))
-                return ts[len(ts) // 2]                       # median, each launch after a cache flush
-
-            t_d = timed(sL, skp, svp)
-            t_0 = timed(0, None, None)
+            moda.moda_fwd(sq, sk, sv, skp, svp, sL, out=so, lse=sl)
+            moda.moda_fwd(sq, sk, sv, None, None, 0, out=so, lse=sl)
+            torch.cuda.synchronize()
+            td, t0 = timed_launches([lambda: moda.moda_fwd(sq, sk, sv, skp, svp, sL, out=so, lse=sl),
+                                     lambda: moda.moda_fwd(sq, sk, sv, None, None, 0, out=so, lse=sl)], reps)
+            t_d = sorted(td)[reps // 2]                        # medians, each launch after a cache flush
+            t_0 = sorted(t0)[reps // 2]
             Fs = useful_flops(sB, sT, sHq, sd, sL)
             sweep[ws["name"]] = {"fwd_ms": t_d, "fwd_ms_L0": t_0, "overhead_vs_L0": t_d / t_0 - 1.0,
                                  "fwd_tflops": Fs / (t_d * 1e-3) / 1e12, "reps": reps}
