@@ -245,3 +245,51 @@ def test_bwd_q8_full_window_is_bwd_q8():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_bwd_q8_workload_sampled():
+    """B = 2, T = 16K workload over 8-bit depth KV: the query and depth-slot
+    gradients of sampled (b, t, kv head) groups against the oracle's
+    per-group form on the dequantised depth KV, and the exact gradient sums
+    (sum of dv over all keys = sum of dout, sum of dk = 0) per (b, kv head)."""
+    w = workload("bf16_B2_T16384_Hq16_Hkv2_d128_L24")
+    _say(f"bwd q8 {w['name']} (sampled groups + gradient sums)")
+    B, T, Hq, Hkv, d, L = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L, dtype=w["dtype"], seed=w["seed"])
+    dout = make_dout(B, T, Hq, d, dtype=w["dtype"], seed=w["seed"])
+    dev = torch.device("cuda:0")
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    packed = moda.moda_pack_depth_q8(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd_q8(qd, ksd, vsd, packed, L)
+    dq, dks, dvs, dkd, dvd = moda.moda_bwd_q8(qd, ksd, vsd, packed, L, out, lse, dd)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    rng = np.random.default_rng(w["seed"] + 13)
+    ts = sorted(set(rng.integers(0, T, 20).tolist()) | {0, 1, 63, T - 1})
+    groups = [(int(rng.integers(0, B)), t, kvh) for t in ts for kvh in range(Hkv)]
+    kdq, vdq = _deq_logical(kd), _deq_logical(vd)
+    rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), kdq, vdq, np32(dout), groups=groups)
+    gq = np.stack([dq[b, t, kvh * G:(kvh + 1) * G].double().cpu().numpy() for (b, t, kvh) in groups])
+    gkd = np.stack([dkd[b, t, :, kvh].double().cpu().numpy() for (b, t, kvh) in groups])
+    gvd = np.stack([dvd[b, t, :, kvh].double().cpu().numpy() for (b, t, kvh) in groups])
+    tol = TOL_BWD[q.dtype]
+
+    def rel(a, r):
+        return float(np.abs(a - r).max()) / max(1.0, float(np.abs(r).max()))
+
+    errs = {"dq": rel(gq, rq), "dk_depth": rel(gkd, rkd), "dv_depth": rel(gvd, rvd)}
+    do = np32(dout).astype(np.float64)
+    dvs_, dks_ = dvs.double().cpu().numpy(), dks.double().cpu().numpy()
+    dvd_, dkd_ = dvd.double().cpu().numpy(), dkd.double().cpu().numpy()
+    for b in range(B):
+        for kvh in range(Hkv):
+            sv = dvs_[b, :, kvh].sum(0) + dvd_[b, :, :, kvh].sum((0, 1))
+            ref = do[b, :, kvh * G:(kvh + 1) * G].sum((0, 1))
+            l1v = np.abs(dvs_[b, :, kvh]).sum(0) + np.abs(dvd_[b, :, :, kvh]).sum((0, 1))
+            sk = dks_[b, :, kvh].sum(0) + dkd_[b, :, :, kvh].sum((0, 1))
+            l1k = np.abs(dks_[b, :, kvh]).sum(0) + np.abs(dkd_[b, :, :, kvh]).sum((0, 1))
+            errs[f"sum_dv[{b},{kvh}]"] = float((np.abs(sv - ref) / l1v).max())
+            errs[f"sum_dk[{b},{kvh}]"] = float((np.abs(sk) / l1k).max())
+    _say(f"{w['name']} q8: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{k} error {v} > {tol}"
