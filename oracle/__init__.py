@@ -8,4 +8,4 @@ from .moda_oracle import (  # noqa: F401
     moda_forward_scalar,
     depth_utilisation,
 )
-from .moda_backward import moda_backward  # noqa: F401
+from .moda_backward import moda_backward, moda_backward_keys  # noqa: F401

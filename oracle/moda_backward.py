@@ -30,8 +30,9 @@ the G heads of one position.
 Parity pins (tests/test_oracle_backward.py): central finite differences of the
 forward oracle, torch autograd of float64 masked attention (a library routine)
 with and without depth, the exact sums sum_j dL/dv_j = sum_i dout_i and
-sum_j dL/dk_j = 0 per kv head, and the sampled-group form against the full
-form.  None of these functions is "parity unpinned".
+sum_j dL/dk_j = 0 per kv head, the sampled-group form against the full form,
+and the per-key form (moda_backward_keys) against the full form.  None of
+these functions is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -132,3 +133,59 @@ def moda_backward(q, k_seq, v_seq, k_depth, v_depth, dout,
                 dvd[b, t, :, kvh] = gvd
     return (dq, np.transpose(dks, (0, 2, 1, 3)).copy(), np.transpose(dvs, (0, 2, 1, 3)).copy(),
             dkd, dvd)
+
+
+def moda_backward_keys(q, k_seq, v_seq, k_depth, v_depth, dout, keys: Sequence[tuple]):
+    """Gradients of selected sequence keys, one key (column) at a time.
+
+    keys = list of (b, s, kvh).  Returns (dk [n,d], dv [n,d]) in that order:
+    dL/dk_seq[b, s, kvh] and dL/dv_seq[b, s, kvh], float64.
+
+    The same derivative as moda_backward, written per key instead of per query
+    group.  Sequence key s of kv head kvh is seen by every row (b, t, h) with
+    t >= s (the causal mask of the mhpn.cn article, section 2.2) and h one of
+    the G query heads of kvh.  For such a row, with its lse and out from the
+    forward oracle,
+        p     = exp(q_row . k_s / sqrt(d) - lse_row)        (its weight on s)
+        Delta = dout_row . out_row   (= sum_j p_j dL/dp_j, because
+                                      out_row = sum_j p_j v_j)
+        dL/dv_s += p * dout_row
+        dL/dk_s += p * (dout_row . v_s - Delta) * q_row / sqrt(d)
+    Only the rows at positions s .. T-1 of the key's own (b, kv head) are
+    evaluated, so the cost is bounded for keys near the end of a long
+    sequence.
+    """
+    from .moda_oracle import moda_forward
+
+    q, k_seq, v_seq = np.asarray(q), np.asarray(k_seq), np.asarray(v_seq)
+    dout = np.asarray(dout)
+    B, T, Hq, d = q.shape
+    Hkv = k_seq.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    keys = [tuple(int(x) for x in k) for k in keys]
+    for (b, s, kvh) in keys:
+        if not (0 <= b < B and 0 <= s < T and 0 <= kvh < Hkv):
+            raise ValueError(f"key {(b, s, kvh)} out of range")
+    # every row that sees at least one selected key: per (b, kv head), the
+    # positions from the earliest selected key to the end, all G heads
+    first = {}
+    for (b, s, kvh) in keys:
+        first[(b, kvh)] = min(s, first.get((b, kvh), T))
+    rows = [(b, t, h) for (b, kvh), s0 in sorted(first.items())
+            for t in range(s0, T) for h in range(kvh * G, (kvh + 1) * G)]
+    out, lse = moda_forward(q, k_seq, v_seq, k_depth, v_depth, rows=rows)
+    at = {r: i for i, r in enumerate(rows)}
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for n, (b, s, kvh) in enumerate(keys):
+        ks_ = _f64(k_seq[b, s, kvh])
+        vs_ = _f64(v_seq[b, s, kvh])
+        idx = [at[(b, t, h)] for t in range(s, T) for h in range(kvh * G, (kvh + 1) * G)]
+        Qr = _f64(q[b, s:, kvh * G:(kvh + 1) * G]).reshape(-1, d)      # rows (t, h), t-major
+        dOr = _f64(dout[b, s:, kvh * G:(kvh + 1) * G]).reshape(-1, d)
+        p = np.exp((Qr @ ks_) * scale - lse[idx])
+        delta = (dOr * out[idx]).sum(axis=1)
+        dv[n] = p @ dOr
+        dk[n] = ((p * (dOr @ vs_ - delta)) @ Qr) * scale
+    return dk, dv

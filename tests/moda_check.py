@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import depth_augmented_attention_amd as moda
-from oracle import moda_forward
+from oracle import moda_backward_keys, moda_forward
 
 # Tolerances on max |gpu - oracle| (out and lse), by input dtype: float32
 # inputs are computed in float32 end to end; bf16 inputs use bf16 matrix-core
@@ -58,3 +58,34 @@ def compare_rows(inputs, out, lse, rows):
         l = lse[bt, ht, tt].to(torch.float64).cpu().numpy()
         err_l = float(np.abs(l - ref_lse).max())
     return err_o, err_l
+
+
+def rel_err(got, ref):
+    """max |got - ref| / max(1, max |ref|): the backward's error measure (sums
+    over many rows, such as the gradients of early keys, grow with T)."""
+    if ref.size == 0:
+        return 0.0
+    return float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
+
+
+def tail_keys(T, last=64, bounds=(128, 256)):
+    """Sequence keys checked element by element at large T: the last `last`
+    keys (the last key tiles and query-row blocks of the dK/dV kernel, at its
+    highest offsets) and the keys on each side of the 128-key tile
+    boundaries T - 128 and T - 256 (and of T rounded down to those tiles)."""
+    ks = set(range(max(0, T - last), T))
+    for bnd in bounds:
+        for edge in (T - bnd, (T - 1) // 128 * 128 - (bnd - 128)):
+            ks |= {edge - 1, edge}
+    return sorted(s for s in ks if 0 <= s < T)
+
+
+def key_errors(tag, q, ks, vs, kd, vd, dout, dks_gpu, dvs_gpu, B, Hkv, keys_s):
+    """max |gpu - oracle| / max(1, max |oracle|) of dk_seq and dv_seq at the
+    given keys of every (b, kv head), against the oracle's per-key form.
+    dks_gpu / dvs_gpu: [B,T,Hkv,d] GPU tensors (or arrays)."""
+    keys = [(b, s, kvh) for b in range(B) for s in keys_s for kvh in range(Hkv)]
+    rk, rv = moda_backward_keys(q, ks, vs, kd, vd, dout, keys=keys)
+    sel = lambda g: np.stack([(g[b, s, kvh].double().cpu().numpy() if torch.is_tensor(g) else g[b, s, kvh])
+                              for (b, s, kvh) in keys])
+    return {f"dk_seq[{tag}]": rel_err(sel(dks_gpu), rk), f"dv_seq[{tag}]": rel_err(sel(dvs_gpu), rv)}

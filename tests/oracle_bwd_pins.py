@@ -19,6 +19,10 @@ What each pin rests on:
                   so the key gradients of one kv head sum to zero.
   groups          The per-group form (query rows and depth slots of one
                   (b, t, kv head)) equals the same entries of the full form.
+  keys            The per-key form (sequence-key gradients summed column by
+                  column over the rows that see the key, through lse and
+                  Delta = dout . out) equals the same entries of the full form,
+                  which the pins above tie to finite differences and autograd.
 """
 from __future__ import annotations
 
@@ -151,6 +155,25 @@ def pin_groups(bwd):
                 float(np.abs(gvd[i] - dvd[b, t, :, kvh]).max()))
         worst = max(worst, e)
         assert e <= 1e-13, f"group {(b, t, kvh)}: {e}"
+    return worst
+
+
+def pin_keys(keys_fn, bwd=None):
+    """keys_fn has the signature of oracle.moda_backward_keys; the full form
+    comes from `bwd` (default: the oracle's moda_backward)."""
+    if bwd is None:
+        from oracle import moda_backward as bwd
+    rng = np.random.default_rng(25)
+    worst = 0.0
+    for (B, T, Hq, Hkv, d, L_d) in [(2, 9, 6, 2, 5, 3), (1, 7, 2, 2, 4, 0), (1, 6, 4, 1, 3, 2)]:
+        *x, dout = _inputs(rng, B, T, Hq, Hkv, d, L_d)
+        _, dks, dvs, _, _ = bwd(*x, dout)
+        keys = [(b, s, kvh) for b in range(B) for s in range(T) for kvh in range(Hkv)]
+        gk, gv = keys_fn(*x, dout, keys=keys)
+        for i, (b, s, kvh) in enumerate(keys):
+            e = max(float(np.abs(gk[i] - dks[b, s, kvh]).max()), float(np.abs(gv[i] - dvs[b, s, kvh]).max()))
+            worst = max(worst, e)
+            assert e <= 1e-12, f"key {(b, s, kvh)} of shape {(B, T, Hq, Hkv, d, L_d)}: {e}"
     return worst
 
 

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import depth_augmented_attention_amd as moda
-from moda_check import np32
+from moda_check import key_errors, np32, rel_err as _rel_err, tail_keys
 from moda_inputs import make_dout, make_inputs, workload
 from oracle import moda_backward
 
@@ -42,12 +42,6 @@ def run_fwd_bwd(q, ks, vs, kd, vd, dout):
     grads = moda.moda_bwd(qd, kd_, vd_, kp, vp, L_d, out, lse, dd)
     torch.cuda.synchronize()
     return [None if g is None else g.double().cpu().numpy() for g in grads]
-
-
-def _rel_err(got, ref):
-    if ref.size == 0:
-        return 0.0
-    return float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
 
 
 def _check_all(name, dtype, got, ref):
@@ -113,9 +107,11 @@ def test_bwd_workload_T4096_all_elements():
                                   "bf16_B1_T65536_Hq32_Hkv1_d128_L48"])
 def test_bwd_workload_sampled(name):
     """At the 16K and 64K workloads: the query and depth-slot gradients of
-    sampled (b, t, kv head) groups against the oracle's per-group form, and
-    the exact sums (sum of dv over all keys = sum of dout; sum of dk = 0) per
-    (batch, kv head)."""
+    sampled (b, t, kv head) groups against the oracle's per-group form, the
+    sequence-key gradients of the last keys and of the keys around the last
+    128-key tile boundaries against its per-key form (every batch and kv
+    head), and the exact sums (sum of dv over all keys = sum of dout; sum of
+    dk = 0) per (batch, kv head)."""
     w = workload(name)
     _say(f"bwd {w['name']} (sampled groups + gradient sums)")
     B, T, Hq, Hkv, d, L_d = w["B"], w["T"], w["Hq"], w["Hkv"], w["d"], w["L_d"]
@@ -133,6 +129,9 @@ def test_bwd_workload_sampled(name):
     gvd = np.stack([dvd[b, t, :, kvh] for (b, t, kvh) in groups])
     tol = TOL_BWD[q.dtype]
     errs = {"dq": _rel_err(gq, rq), "dk_depth": _rel_err(gkd, rkd), "dv_depth": _rel_err(gvd, rvd)}
+    # sequence-key gradients element by element at the last keys (both batches)
+    errs.update(key_errors("tail", np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), dks, dvs, B, Hkv,
+                           tail_keys(T)))
     # exact sums, checked relative to the L1 size of the summands
     do = np32(dout).astype(np.float64)
     for b in range(B):
@@ -152,8 +151,8 @@ def test_bwd_workload_sampled(name):
 def test_bwd_long_sequence():
     """T * Hq * d * 2 bytes = 2^31 (past 32-bit byte offsets from the batch's
     first row; G = 32 divides the 64-row blocks, so the dK/dV kernel addresses
-    rows from each block's base): sampled groups against the oracle and the
-    exact gradient sums."""
+    rows from each block's base): sampled groups against the oracle, the last
+    sequence keys element by element, and the exact gradient sums."""
     B, T, Hq, Hkv, d, L_d = 1, 262144, 32, 1, 128, 2
     _say(f"bwd long sequence B{B} T{T} Hq{Hq} Hkv{Hkv} d{d} L{L_d}")
     q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype="bf16", seed=77)
@@ -175,6 +174,9 @@ def test_bwd_long_sequence():
     gkd = dkd[0].index_select(0, idx)[:, :, 0].double().cpu().numpy()  # [n, L_d, d]
     gvd = dvd[0].index_select(0, idx)[:, :, 0].double().cpu().numpy()
     errs = {"dq": _rel_err(gq, rq), "dk_depth": _rel_err(gkd, rkd), "dv_depth": _rel_err(gvd, rvd)}
+    # the last keys (highest q / dO offsets of the dK/dV kernel) element by element
+    errs.update(key_errors("tail", np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), dks, dvs, B, Hkv,
+                           tail_keys(T, last=32, bounds=(128,))))
     dvs_, dks_ = dvs[0, :, 0].double().cpu().numpy(), dks[0, :, 0].double().cpu().numpy()
     dvd_, dkd_ = dvd[0, :, :, 0].double().cpu().numpy(), dkd[0, :, :, 0].double().cpu().numpy()
     ref = dout[0].sum((0, 1), dtype=torch.float64).numpy()

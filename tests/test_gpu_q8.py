@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import depth_augmented_attention_amd as moda
-from moda_check import TOL, np32
+from moda_check import TOL, key_errors, np32, tail_keys
 from moda_inputs import make_dout, make_inputs, sample_rows, workload
 from oracle import moda_backward, moda_forward
 from oracle.moda_quant import dequantize_rows, quantize_rows
@@ -250,7 +250,8 @@ def test_bwd_q8_full_window_is_bwd_q8():
 def test_bwd_q8_workload_sampled():
     """B = 2, T = 16K workload over 8-bit depth KV: the query and depth-slot
     gradients of sampled (b, t, kv head) groups against the oracle's
-    per-group form on the dequantised depth KV, and the exact gradient sums
+    per-group form on the dequantised depth KV, the sequence-key gradients of
+    the last keys against its per-key form, and the exact gradient sums
     (sum of dv over all keys = sum of dout, sum of dk = 0) per (b, kv head)."""
     w = workload("bf16_B2_T16384_Hq16_Hkv2_d128_L24")
     _say(f"bwd q8 {w['name']} (sampled groups + gradient sums)")
@@ -278,6 +279,9 @@ def test_bwd_q8_workload_sampled():
         return float(np.abs(a - r).max()) / max(1.0, float(np.abs(r).max()))
 
     errs = {"dq": rel(gq, rq), "dk_depth": rel(gkd, rkd), "dv_depth": rel(gvd, rvd)}
+    # sequence-key gradients element by element at the last keys (both batches)
+    errs.update(key_errors("tail", np32(q), np32(ks), np32(vs), kdq, vdq, np32(dout), dks, dvs, B, Hkv,
+                           tail_keys(T)))
     do = np32(dout).astype(np.float64)
     dvs_, dks_ = dvs.double().cpu().numpy(), dks.double().cpu().numpy()
     dvd_, dkd_ = dvd.double().cpu().numpy(), dkd.double().cpu().numpy()
