@@ -76,8 +76,24 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inputs, budget_s):
-    """Oracle rate on a bounded, seeded sample of query rows of the workload."""
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
+def cpu_baseline(w, inputs, budget_s, out_cpu=None, lse_cpu=None):
+    """Oracle rate on a bounded, seeded sample of query rows of the workload.
+
+    When the timed forward's out / lse (CPU copies) are given, the sampled
+    rows are also compared with them: max |out - oracle| and max |lse - oracle|
+    over those rows."""
     import numpy as np
     import torch
 
@@ -85,35 +101,93 @@ def cpu_baseline(w, inputs, budget_s):
     from oracle import moda_forward
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = None
+    cores = len(os.sched_getaffinity(0))
     q, ks, vs, kd, vd = [x.to(torch.float32).numpy() for x in inputs]
-    rows = sample_rows(w["B"], w["T"], w["Hq"], n=65536, seed=w["seed"] + 11)
+    B, T, Hq, L_d = w["B"], w["T"], w["Hq"], w["L_d"]
+    rows = sample_rows(B, T, Hq, n=65536, seed=w["seed"] + 11)
     rng = np.random.default_rng(w["seed"] + 12)
     rows = rows[rng.permutation(len(rows))]
     done = 0
     flops = 0.0
+    err_o = err_l = 0.0
     c0 = time.process_time()
     t0 = time.perf_counter()
     chunk = 64
     while done < len(rows) and time.perf_counter() - t0 < budget_s:
         sel = rows[done:done + chunk]
-        moda_forward(q, ks, vs, kd, vd, rows=sel)
-        flops += useful_flops(w["B"], w["T"], w["Hq"], w["d"], w["L_d"], rows=sel)
+        ro, rl = moda_forward(q, ks, vs, kd, vd, rows=sel)
+        if out_cpu is not None:
+            b_, t_, h_ = sel[:, 0], sel[:, 1], sel[:, 2]
+            err_o = max(err_o, float(np.abs(out_cpu[b_, t_, h_].astype(np.float64) - ro).max()))
+            err_l = max(err_l, float(np.abs(lse_cpu[b_, h_, t_].astype(np.float64) - rl).max()))
+        flops += useful_flops(B, T, Hq, w["d"], L_d, rows=sel)
         done += len(sel)
     dt = time.perf_counter() - t0
     busy = (time.process_time() - c0) / dt      # CPU seconds per wall second, all threads
-    return {
+    # the oracle's cost of a row is proportional to its key count t + 1 + L_d
+    keys_done = float(sum(int(t) + 1 + L_d for t in rows[:done, 1]))
+    keys_all = float(B * Hq) * (T * (T + 1) / 2 + T * L_d)
+    res = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{done} seeded random (b,t,h) query rows of {w['name']} "
                   f"(float64 numpy oracle, {dt:.1f} s; rate = useful FLOPs of those rows / time)",
+        "cpu_model": cpu_model(),
+        "blas_threads": blas,
         "rows_per_s": done / dt,
         "cpu_seconds_per_wall_second": busy,
+        "projected_full_output_s": dt * keys_all / keys_done,
+        "projection": "measured time x (keys of all rows) / (keys of the sampled rows): a projection, not a run",
     }
+    if out_cpu is not None:
+        res["max_abs_err_out"] = err_o
+        res["max_abs_err_lse"] = err_l
+        res["err_rows"] = done
+    return res
+
+
+def gpu_clock_under_load(launch, seconds=2.5):
+    """sclk (MHz) that rocm-smi reports while `launch` keeps the GPU busy
+    (enough launches queued for about `seconds`), and the highest sclk level."""
+    import subprocess
+
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    launch()
+    ev[1].record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds * 1e3 / max(ev[0].elapsed_time(ev[1]), 1e-3)))
+    for _ in range(n):
+        launch()
+    time.sleep(0.4)
+    cur = top = None
+    try:
+        import re
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            m = re.search(r"(\d+)\s*Mhz", line)
+            if "sclk" in line and m:
+                cur = float(m.group(1))
+                break
+        r = subprocess.run(["rocm-smi", "--showclkfrq"], capture_output=True, text=True, timeout=20)
+        sec = False
+        for line in r.stdout.splitlines():
+            if "frequencies" in line:
+                sec = "sclk" in line.lower()
+                continue
+            m = re.search(r"(\d+)\s*Mhz", line)
+            if sec and m:
+                top = max(top or 0.0, float(m.group(1)))
+    except Exception:  # pragma: no cover
+        pass
+    torch.cuda.synchronize()
+    return cur, top
 
 
 def main():
@@ -195,6 +269,10 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     avg_fwd = sum(fwd_ms) / len(fwd_ms)
     avg_pack = sum(pack_ms) / len(pack_ms)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    # the timed forward's results, compared with the oracle's sampled rows below
+    out_cpu = out.to(torch.float32).cpu().numpy() if not args.no_cpu_baseline else None
+    lse_cpu = lse.cpu().numpy() if not args.no_cpu_baseline else None
     F = useful_flops(B, T, Hq, d, L_d)
     log(f"step {ms_per_step:.3f} ms  fwd {avg_fwd:.3f} ms  pack {avg_pack:.3f} ms")
 
@@ -228,7 +306,10 @@ def main():
         "avg_launch_ms": avg_fwd,
     }
     res["fwd_ms"] = avg_fwd
+    res["fwd_ms_median"] = med(fwd_ms)
+    res["step_ms_median"] = med([a + b for a, b in zip(pack_ms, fwd_ms)])
     res["fwd_tflops"] = fwd_tflops
+    res["fwd_tflops_median"] = F / (med(fwd_ms) * 1e-3) / 1e12
     res["pct_mfma_peak"] = 100.0 * fwd_tflops / peak
     res["pack_ms"] = avg_pack
     res["pack_gbps"] = 2 * 2 * kd.numel() * kd.element_size() / (avg_pack * 1e-3) / 1e9
@@ -269,6 +350,9 @@ def main():
         avg_ld = sum(ld) / len(ld)
         res["fwd_ms_L0"] = avg_l0
         res["fwd_ms_flushed"] = avg_ld
+        res["fwd_ms_L0_median"] = med(l0)
+        res["fwd_ms_flushed_median"] = med(ld)
+        res["overhead_vs_L0_median"] = med(ld) / med(l0) - 1.0
         res["fwd_tflops_L0"] = useful_flops(B, T, Hq, d, 0) / (avg_l0 * 1e-3) / 1e12
         res["overhead_vs_L0"] = avg_ld / avg_l0 - 1.0
         res["overhead_vs_L0_with_pack"] = (avg_ld + avg_pack) / avg_l0 - 1.0
@@ -390,6 +474,47 @@ def main():
             del sq, sk, sv, skd, svd, skp, svp, so, sl
         res["overhead_sweep"] = sweep
 
+    if not args.no_sweep and w["dtype"] == "bf16":
+        # depth sweep at the bench shape: the same kernel with L_d = 0, 12, 24
+        # and 48 slots (inputs N(0,1) drawn on the GPU: timing only), launches
+        # of the four taken in turn, each after the cache fill; medians
+        log("depth sweep L_d = 0, 12, 24, 48")
+        g = torch.Generator(device=dev).manual_seed(w["seed"] + 99)
+        Lmax = 48
+        kdx = torch.randn(B, T, Lmax, Hkv, d, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+        vdx = torch.randn(B, T, Lmax, Hkv, d, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+        packs = {}
+        for Lx in (12, 24, 48):
+            packs[Lx] = moda.moda_pack_depth(kdx[:, :, :Lx].contiguous(), vdx[:, :, :Lx].contiguous())
+        del kdx, vdx
+        fns = [lambda: moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)]
+        for Lx in (12, 24, 48):
+            fns.append(lambda Lx=Lx: moda.moda_fwd(q, ks, vs, packs[Lx][0], packs[Lx][1], Lx, out=out, lse=lse))
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        times = timed_launches(fns, 5)
+        t0m = med(times[0])
+        dsw = {"L_d": [0, 12, 24, 48], "fwd_ms_median": [med(t) for t in times],
+               "overhead_vs_L0": [med(t) / t0m - 1.0 for t in times]}
+        # least-squares line through the added time: linear in L_d if the
+        # residuals are small against the slope
+        xs = [0.0, 12.0, 24.0, 48.0]
+        ys = [med(t) - t0m for t in times]
+        xm, ym = sum(xs) / 4, sum(ys) / 4
+        slope = sum((x - xm) * (y - ym) for x, y in zip(xs, ys)) / sum((x - xm) ** 2 for x in xs)
+        dsw["added_ms_per_slot"] = slope
+        dsw["fit_residual_ms_max"] = max(abs(y - (ym + slope * (x - xm))) for x, y in zip(xs, ys))
+        res["depth_sweep"] = dsw
+        del packs
+        log("depth sweep: " + ", ".join(f"L{x} {y:.3f} ms" for x, y in zip(dsw["L_d"], dsw["fwd_ms_median"])))
+        # the clock the forward runs at: rocm-smi's sclk while the forward
+        # keeps the GPU busy
+        cur, top = gpu_clock_under_load(lambda: moda.moda_fwd(q, ks, vs, kp, vp, L_d, out=out, lse=lse))
+        res["gpu_sclk_mhz_under_load"] = cur
+        res["gpu_sclk_mhz_max"] = top
+        log(f"sclk under load {cur} MHz (max {top} MHz)")
+
     if not args.no_bwd:
         # backward of the same forward: dq, dk/dv of sequence and depth keys
         from moda_inputs import make_dout
@@ -418,7 +543,9 @@ def main():
     if not args.no_cpu_baseline:
         log(f"oracle on host cores ({args.cpu_budget:.0f} s budget)")
         del q, ks, vs, kd, vd
-        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget, out_cpu, lse_cpu)
+        res["max_abs_err_out"] = res["cpu_baseline"].get("max_abs_err_out")
+        res["max_abs_err_lse"] = res["cpu_baseline"].get("max_abs_err_lse")
     else:
         res["cpu_baseline"] = None
     res["kernel_source_hash"] = kernel_source_hash()

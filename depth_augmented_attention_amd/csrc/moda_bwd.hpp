@@ -187,9 +187,16 @@ __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = reg_key(r, hh);
-      const float pr = __builtin_amdgcn_exp2f((key >= own_lo && key < own_hi) ? s[r] * sl2 - lse2 : -INFINITY);
-      ds[r] = pr * (dp[r] - dlt);
+      const bool own = key >= own_lo && key < own_hi;
+      const float pr = __builtin_amdgcn_exp2f(own ? s[r] * sl2 - lse2 : -INFINITY);
+      // a masked key contributes exactly 0 (its dP may be non-finite when the
+      // slot is unread)
+      ds[r] = own ? pr * (dp[r] - dlt) : 0.f;
     }
+    // keys of unread slots (and padding) are zeroed in the dQ operand: their
+    // dS is 0, and 0 * x would still carry a non-finite x into dQ
+    const uint32_t rows_ok = depth_tile_partial(n0, L_cap, slot_lo, L_d, p.T)
+                                 ? depth_tile_rows(n0, L_cap, slot_lo, L_d, p.T, n + 32 * hh) : 0xffffffffu;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       Frag f;
@@ -201,6 +208,7 @@ __device__ __forceinline__ void dq_depth_fold(const BwdParams& p, int bh, int tw
         for (int j = 0; j < 8; ++j) {
           const long long r = n0 + c * 16 + hh * 8 + j;
           kt[j] = p.q8 ? Dequant<E>::one(kq8[r * D + dt * 32 + n], ks8[r]) : kdb[r * D + dt * 32 + n];
+          if (!((rows_ok >> (c * 16 + hh * 8 + j)) & 1u)) kt[j] = (E)0.f;
         }
         acc[dt] = mma16(kt, f, acc[dt]);
       }

@@ -60,6 +60,23 @@ __device__ __forceinline__ bool depth_tile_used(long long n0, int L_cap, int slo
   return w0 < n0 + 32 && w0 + L_d > n0;
 }
 
+// Rows of the 32-key depth tile at packed key n0 that hold a slot of the
+// window [slot_lo, slot_lo + L_d) of a position t < T: bit r for key n0 + r
+// (a wave-wide vote; n0 + 31 < 2^31, checked at the boundary).  Every row
+// outside the window gets probability 0, but 0 * x is NaN for a non-finite x,
+// so the values (and, in the backward, the keys) of unread slots and of the
+// padding rows past T * L_cap are zeroed before they reach a product.  Only
+// needed when the window leaves slots out or the tile runs past the last key.
+__device__ __forceinline__ bool depth_tile_partial(long long n0, int L_cap, int slot_lo, int L_d, int T) {
+  return slot_lo != 0 || L_d != L_cap || n0 + 32 > (long long)T * L_cap;
+}
+__device__ __forceinline__ uint32_t depth_tile_rows(long long n0, int L_cap, int slot_lo, int L_d, int T, int lane) {
+  const uint32_t n = (uint32_t)n0 + (uint32_t)(lane & 31);
+  const uint32_t slot = n % (uint32_t)L_cap;
+  const bool ok = n / (uint32_t)L_cap < (uint32_t)T && slot - (uint32_t)slot_lo < (uint32_t)L_d;
+  return (uint32_t)__ballot(ok);
+}
+
 // Query tile of workgroup slot s = blockIdx / (B * Hkv).  Longest tiles
 // (latest positions, most keys) first; with `paired` set (a grid that the GPU
 // runs in at most two rounds, two workgroups per compute unit) the second
@@ -298,6 +315,10 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
         sv[r] = (key >= own_lo && key < own_hi) ? acc[r] * sl2 : -INFINITY;
       }
       online_update<E>(sv, m_run, l_run, o);
+      // rows of this tile that may be read (all of them unless the window
+      // leaves slots out or the tile runs past the last key)
+      const uint32_t rows_ok = depth_tile_partial(n0, L_cap, slot_lo, L_d, T)
+                                   ? depth_tile_rows(n0, L_cap, slot_lo, L_d, T, lane) : 0xffffffffu;
       // V^T operand: 8 consecutive keys of head dimension dt*32 + n, gathered
       // from the key-major packed rows
 #pragma unroll
@@ -316,6 +337,7 @@ __global__ __launch_bounds__(NW * 64) void moda_fwd_kernel(FwdParams p) {
             } else {
               vt[j] = vdb[key * D + dt * 32 + n];
             }
+            if (!((rows_ok >> (c * 16 + hh * 8 + j)) & 1u)) vt[j] = (E)0.f;
           }
           o[dt] = mma16(vt, pf, o[dt]);
         }

@@ -400,6 +400,14 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) acc = mma16(kfr[kc], qf[kc], acc);
+      // value rows of unread slots (and padding) are zeroed: their weight is
+      // 0, and 0 * x would still carry a non-finite x into O
+      if (depth_tile_partial(n0, L_cap, slot_lo, L_d, T)) {
+        const uint32_t rows_ok = depth_tile_rows(n0, L_cap, slot_lo, L_d, T, lane) >> (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (!((rows_ok >> (4 * i)) & 1u)) vr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
       // the value rows go to this wave's LDS region with the V-stage swizzle,
       // to be read back with the same transpose reads as the sequence blocks
 #pragma unroll

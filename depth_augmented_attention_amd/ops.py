@@ -117,8 +117,7 @@ def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
 
     Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
     """
-    return moda_fwd_window(q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out=out, lse=lse,
-                           with_lse=with_lse, stream=stream)
+    return _fwd_call("moda_fwd", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, with_lse, stream)
 
 
 def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
@@ -131,6 +130,13 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
 
     Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
     """
+    return _fwd_call("moda_fwd_window", q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse,
+                     with_lse, stream)
+
+
+def _fwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse, with_lse, stream):
+    """Checks and the call of moda_fwd (fn = "moda_fwd": L_cap slots, all
+    read) or moda_fwd_window (fn = "moda_fwd_window")."""
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
     B, T, Hq, d = q.shape
@@ -163,11 +169,12 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
     dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse)
-    st = _call(dev, "moda_fwd_window", stream,
+    slots = (L_cap,) if fn == "moda_fwd" else (L_cap, slot_lo, slot_hi)
+    st = _call(dev, fn, stream,
         q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
         out.data_ptr(), lse.data_ptr() if lse is not None else None,
-        B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi, _dtype_code(q))
-    check(st, "moda_fwd_window")
+        B, T, Hq, Hkv, d, *slots, _dtype_code(q))
+    check(st, fn)
     return out, lse
 
 
@@ -185,8 +192,8 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     L_d == 0.  `grads` may supply those five output tensors; `work` a float32
     [2,B,Hq,T] scratch tensor.
     """
-    return moda_bwd_window(q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, dout,
-                           grads=grads, work=work, stream=stream)
+    return _bwd_call("moda_bwd", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, dout, grads, work,
+                     stream)
 
 
 def _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout, grads, work):
@@ -237,6 +244,14 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     """Gradients of moda_fwd_window(..., L_cap, slot_lo, slot_hi): as
     moda_bwd, with the depth gradients of slots slot_lo .. slot_hi-1
     ([B,T,slot_hi-slot_lo,Hkv,d])."""
+    return _bwd_call("moda_bwd_window", q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse,
+                     dout, grads, work, stream)
+
+
+def _bwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse, dout, grads, work,
+              stream):
+    """Checks and the call of moda_bwd (fn = "moda_bwd": L_cap slots, all
+    read) or moda_bwd_window."""
     (B, T, Hq, Hkv, d, L_d), grads, work = _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout,
                                                        grads, work)
     kd_ptr = vd_ptr = None
@@ -252,12 +267,13 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     ptr = [g.data_ptr() if g is not None else None for g in grads]
     dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
                       dout, work, *grads[:3], *(grads[3:] if L_d > 0 else ()))
-    st = _call(dev, "moda_bwd_window", stream,
+    slots = (L_cap,) if fn == "moda_bwd" else (L_cap, slot_lo, slot_hi)
+    st = _call(dev, fn, stream,
         q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
-        ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, L_cap, slot_lo, slot_hi,
+        ptr[3], ptr[4], work.data_ptr(), B, T, Hq, Hkv, d, *slots,
         _dtype_code(q))
-    check(st, "moda_bwd_window")
+    check(st, fn)
     return grads
 
 
