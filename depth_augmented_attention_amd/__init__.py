@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
 )
 from .ops import (  # noqa: F401
     depth_packed_elems,
+    fwd_workspace,
+    fwd_workspace_bytes,
     moda_append_depth,
     moda_append_depth_q8,
     moda_bwd,

@@ -16,9 +16,11 @@ MODA_ERR_SHAPE = 2
 MODA_ERR_DTYPE = 3
 MODA_ERR_UNSUPPORTED = 4
 MODA_ERR_HIP = 5
+MODA_ERR_WORKSPACE = 6
 
 # every symbol include/moda.h declares
-EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_window",
+EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_workspace_bytes", "moda_fwd_ws",
+           "moda_fwd_window",
            "moda_append_depth", "moda_bwd", "moda_bwd_window", "moda_pack_depth_q8", "moda_fwd_q8",
            "moda_fwd_window_q8", "moda_append_depth_q8", "moda_bwd_q8", "moda_bwd_window_q8",
            "moda_status_string")
@@ -50,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.moda_pack_depth.restype = c_int
     lib.moda_fwd.argtypes = [c_vp] * 6 + [c_vp] + [c_int] * 7 + [c_vp]
     lib.moda_fwd.restype = c_int
+    lib.moda_fwd_workspace_bytes.argtypes = [c_int] * 6
+    lib.moda_fwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.moda_fwd_ws.argtypes = [c_vp] * 6 + [c_vp] + [c_int] * 7 + [c_vp, ctypes.c_longlong, c_vp]
+    lib.moda_fwd_ws.restype = c_int
     lib.moda_fwd_window.argtypes = [c_vp] * 6 + [c_vp] + [c_int] * 9 + [c_vp]
     lib.moda_fwd_window.restype = c_int
     lib.moda_append_depth.argtypes = [c_vp] * 4 + [c_int] * 7 + [c_vp]

@@ -31,10 +31,39 @@ long long padded_depth_keys(int T, int L_d) {
   return (n + 31) / 32 * 32;
 }
 
+// Split key ranges for the bf16 d = 128 kernel on grids of at most two
+// workgroups per compute unit (four-wave tiles): the longest half of the
+// query tiles of each (b, kv head) is swept by two workgroups each (see
+// moda_fwd_bf16.hpp).  Workspace: the arrival counters in a header of fixed
+// size (the most (split tile, wave) pairs any shape has: a grid of at most
+// 2 * kCUs tiles splits at most kCUs of them, 4 waves each), so that the
+// counters of one shape never overlap the partial states of another that
+// used the same workspace before; then the partial states of both parts of
+// every wave.
+constexpr long long kSplitCntBytes = 2 * kCUs / 2 * 4 * 4;
+struct SplitPlan {
+  int nsplit = 0;          // split tiles per (b, kv head)
+  long long cnt_bytes = 0; // counter header
+  long long bytes = 0;     // whole workspace
+};
+SplitPlan split_plan(int dtype, int d, long long rows, long long BH) {
+  SplitPlan sp;
+  if (fwd_waves(dtype, d, rows, BH) != 4 || dtype != MODA_BF16 || d != 128) return sp;
+  const long long ntiles = (rows + 127) / 128;
+  if (ntiles * BH > 2 * kCUs || ntiles < 2) return sp;
+  sp.nsplit = (int)(ntiles / 2);
+  const long long units = BH * sp.nsplit * 4;    // (split tile, wave) pairs, <= kSplitCntBytes / 4
+  sp.cnt_bytes = kSplitCntBytes;
+  sp.bytes = sp.cnt_bytes + units * 2 * moda::kSplitState * 64 * 4;
+  return sp;
+}
+
 template <typename E, int D>
 hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, int nw, hipStream_t s) {
   if constexpr (sizeof(E) == 2 && D == 128) {
-    if (nw == 8)
+    if (p.nsplit > 0)
+      hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 4, true>), dim3(grid), dim3(4 * 64), 0, s, p);
+    else if (nw == 8)
       hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 8>), dim3(grid), dim3(8 * 64), 0, s, p);
     else
       hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 4>), dim3(grid), dim3(4 * 64), 0, s, p);
@@ -110,6 +139,8 @@ const char* moda_status_string(int status) {
     case MODA_ERR_DTYPE: return "MODA_ERR_DTYPE: unknown dtype";
     case MODA_ERR_UNSUPPORTED: return "MODA_ERR_UNSUPPORTED: head size must be 64 or 128";
     case MODA_ERR_HIP: return "MODA_ERR_HIP: the HIP runtime reported an error";
+    case MODA_ERR_WORKSPACE:
+      return "MODA_ERR_WORKSPACE: the workspace is NULL, misaligned or smaller than moda_fwd_workspace_bytes";
     default: return "unknown moda_status";
   }
 }
@@ -143,7 +174,7 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
 static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                     const void* v_depth, const float* k_scale, const float* v_scale, int q8, void* out,
                     float* lse, int B, int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi,
-                    int dtype, void* stream) {
+                    int dtype, void* stream, void* work = nullptr, long long work_bytes = 0) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
@@ -174,11 +205,25 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.paired = grid <= 2 * kCUs && B * Hkv <= kCUs && kCUs % (B * Hkv) == 0;
   p.NKp = padded_depth_keys(T, L_cap);
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  p.nsplit = 0;
+  p.ws = nullptr;
+  p.cnt = nullptr;
+  long long launch_grid = grid;
+  if (work) {
+    const SplitPlan sp = split_plan(dtype, d, rows, (long long)B * Hkv);
+    if (sp.nsplit > 0) {
+      if (work_bytes < sp.bytes || (reinterpret_cast<uintptr_t>(work) & 255)) return MODA_ERR_WORKSPACE;
+      p.nsplit = sp.nsplit;
+      p.cnt = reinterpret_cast<uint32_t*>(work);
+      p.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(work) + sp.cnt_bytes);
+      launch_grid = (ntiles + sp.nsplit) * B * Hkv;
+    }
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == MODA_BF16)
-    e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)grid, nw, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, nw, s);
+    e = d == 128 ? launch_fwd<moda::bf16, 128>(p, (unsigned)launch_grid, nw, s) : launch_fwd<moda::bf16, 64>(p, (unsigned)grid, nw, s);
   else
     e = d == 128 ? launch_fwd<float, 128>(p, (unsigned)grid, nw, s) : launch_fwd<float, 64>(p, (unsigned)grid, nw, s);
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
@@ -264,6 +309,21 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   if (L_d < 0) return MODA_ERR_SHAPE;
   return moda_fwd_window(q, k_seq, v_seq, k_depth, v_depth, out, lse, B, T, Hq, Hkv, d, L_d, 0, L_d,
                          dtype, stream);
+}
+
+long long moda_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int dtype) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv != 0) return -1;
+  if (!valid_dtype(dtype)) return -1;
+  return split_plan(dtype, d, (long long)T * (Hq / Hkv), (long long)B * Hkv).bytes;
+}
+
+int moda_fwd_ws(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                const void* v_depth, void* out, float* lse, int B, int T, int Hq, int Hkv, int d,
+                int L_d, int dtype, void* work, long long work_bytes, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  if (!work) return MODA_ERR_WORKSPACE;
+  return fwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, B, T, Hq, Hkv, d, L_d, 0,
+                  L_d, dtype, stream, work, work_bytes);
 }
 
 int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void* v_packed, int B,

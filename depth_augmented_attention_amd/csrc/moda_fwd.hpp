@@ -48,6 +48,14 @@ struct FwdParams {
   int paired;       // tile order for grids of at most two rounds (query_tile)
   long long NKp;    // padded depth keys per (b, kvh)
   float scale_log2; // log2(e) / sqrt(d)
+  // split key ranges (bf16 fast path on small grids only; see
+  // moda_fwd_bf16.hpp): the nsplit longest query tiles of each (b, kvh) are
+  // swept by two workgroups, each over part of the key blocks, whose partial
+  // states meet in `ws`; `cnt` counts the arrivals per (split tile, wave) and
+  // is zero before and after every launch.
+  int nsplit;       // split tiles per (b, kvh); 0: every tile is whole
+  float* ws;        // [BH * nsplit][2 parts][NW waves][66][64] float32 partial states
+  uint32_t* cnt;    // [BH * nsplit][NW] arrival counters
 };
 
 // Whether the 32 packed depth keys [n0, n0 + 32) hold any slot of the window

@@ -39,6 +39,22 @@
 //     one 32-key depth tile at a time, with the tile's key fragments and
 //     value rows loaded together (one round trip to memory per tile) and the
 //     values transposed through the wave's own LDS region.
+//   * Split key ranges (SPLIT, four-wave tiles, grids of at most two
+//     workgroups per compute unit): a causal grid's longest tile sweeps about
+//     twice the key blocks of the average one, and on a small grid it alone
+//     sets the time.  With a workspace, each of the nsplit longest tiles of a
+//     (b, kv head) -- tile i, paired with the short tile j = ntiles - 1 - i --
+//     is swept by two workgroups: part 0 over key blocks [0, h), part 1 over
+//     [h, nb_i) plus the depth slots, h = (nb_i - nb_j) / 2.  Parts run
+//     first, then the short tiles longest first; a compute unit whose part 0
+//     ends early takes the next short tile, so part 0 + short tile and part 1
+//     each come to about (nb_i + nb_j) / 2 blocks.  Each wave of a part writes
+//     its running state (O, m, l per lane) to the workspace, and the second
+//     wave of the pair to arrive (a device-wide counter) merges the other's
+//     state into its own -- m = max(m0, m1), O = 2^(m0 - m) O0 + 2^(m1 - m) O1,
+//     l likewise: the same online-softmax recurrence over the union of the
+//     two key sets, exact in real arithmetic -- writes out and lse, and
+//     clears the counter for the next launch.
 #pragma once
 
 #include "moda_common.hpp"
@@ -74,8 +90,13 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* p) {
   return *reinterpret_cast<const bf16x8*>(pr);
 }
 
-// NW waves per workgroup (32 query rows each): 8, or 4 for small grids.
-template <int D, int NW>
+// Floats of one wave's partial state in the split-key workspace: 64 O^T
+// accumulator values, m and l for each of the 64 lanes.
+constexpr int kSplitState = 66;
+
+// NW waves per workgroup (32 query rows each): 8, or 4 for small grids;
+// SPLIT: key ranges of the longest tiles split over two workgroups.
+template <int D, int NW, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moda_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 128, "the bf16 fast path is built for head size 128");
@@ -107,7 +128,19 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH;
-  const int tile = query_tile((int)(blockIdx.x / BH), p.ntiles, p.paired);
+  // part 0 / 1 of a split tile, or -1 for a whole tile
+  int tile, part = -1;
+  if constexpr (SPLIT) {
+    const int slot = (int)(blockIdx.x / BH), H = p.nsplit;
+    if (slot < 2 * H) {
+      part = slot < H ? 1 : 0;
+      tile = p.ntiles - 1 - (slot < H ? slot : slot - H);
+    } else {
+      tile = p.ntiles - 1 - H - (slot - 2 * H);
+    }
+  } else {
+    tile = query_tile((int)(blockIdx.x / BH), p.ntiles, p.paired);
+  }
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;
@@ -129,6 +162,19 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int nblocks = t_last / BN + 1;
   // blocks [0, jm) have every key <= every row's position: no mask needed
   const int jm = (t_first + 1) / BN < nblocks ? (t_first + 1) / BN : nblocks;
+  // key blocks [jlo, jhi) swept by this workgroup
+  int jlo = 0, jhi = nblocks;
+  if constexpr (SPLIT) {
+    if (part >= 0) {
+      const int j_tile = p.ntiles - 1 - tile;          // the short partner tile
+      const long long Rj = ((long long)j_tile + 1) * (NW * 32);
+      const int nbj = (int)(((Rj < TG ? Rj : TG) - 1) / G) / BN + 1;
+      int h = (nblocks - nbj) / 2;
+      h = h < 0 ? 0 : (h > jm ? jm : h);
+      if (part == 0) jhi = h;
+      else jlo = h;
+    }
+  }
 
   bf16x8 qf[NKC];
   {
@@ -183,7 +229,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
       if (sp >= s_lo && sp < s_hi) dma16(rs, off[i], lbase + (sp - sp0) * 512);
     }
   };
-  const int klast = nblocks - 1;
+  const int klast = jhi - 1;
   auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
   // K stage st, half h (rows 32h .. 32h+31 of the block)
   auto khalf = [&](int st, int h) -> bf16* {
@@ -293,16 +339,20 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
   };
 
-  // ---- prologue: K(0) both halves, K(1) first half, V(0) ----
-  dma_rows(kbase, 0, offk, khalf(0, 0), 0, 8, 0);
-  dma_rows(kbase, 0, offk, khalf(0, 1), 8, 16, 8);
-  dma_rows(kbase, clampb(1), offk, khalf(1, 0), 0, 8, 0);
-  dma_rows(vbase, 0, offv, vst(0), 0, 16, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // ---- prologue: K(jlo) both halves, K(jlo+1) first half, V(jlo) ----
+  // (stage of block j: (j - jlo) & 1)
+  const bool sweep = jlo < jhi;                     // workgroup-uniform
   float s_a[16], s_b[16];
-  qk.template operator()<0, 0>(s_a);
-  __syncthreads();   // every wave has read K(0) rows 0-31 before K(2) overwrites them
+  if (sweep) {
+    dma_rows(kbase, jlo, offk, khalf(0, 0), 0, 8, 0);
+    dma_rows(kbase, jlo, offk, khalf(0, 1), 8, 16, 8);
+    dma_rows(kbase, clampb(jlo + 1), offk, khalf(1, 0), 0, 8, 0);
+    dma_rows(vbase, jlo, offv, vst(0), 0, 16, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    qk.template operator()<0, 0>(s_a);
+    __syncthreads();   // every wave has read K(jlo) rows 0-31 before K(jlo+2) overwrites them
+  }
 
   // One 64-key block j (ST = j & 1): half 0 (scores in s_a), half 1 (s_b).
   //   loads:  K(j+2) rows 0-31 -> K stage ST,   K(j+1) rows 32-63 -> K stage ST^1,
@@ -330,21 +380,22 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 1 < jm; j += 2) {
+  const int jmm = jm < jhi ? jm : jhi;   // unmasked blocks of this range end here
+  int j = jlo;
+  for (; j + 1 < jmm; j += 2) {
     block.template operator()<false, 0>(j);
     block.template operator()<false, 1>(j + 1);
   }
-  if (j < jm) { block.template operator()<false, 0>(j); ++j; }
-  if (j < nblocks && (j & 1)) { block.template operator()<true, 1>(j); ++j; }
-  for (; j + 1 < nblocks; j += 2) {
+  if (j < jmm) { block.template operator()<false, 0>(j); ++j; }
+  if (j < jhi && ((j - jlo) & 1)) { block.template operator()<true, 1>(j); ++j; }
+  for (; j + 1 < jhi; j += 2) {
     block.template operator()<true, 0>(j);
     block.template operator()<true, 1>(j + 1);
   }
-  if (j < nblocks) { block.template operator()<true, 0>(j); ++j; }
+  if (j < jhi) { block.template operator()<true, 0>(j); ++j; }
 
   // ---- depth fold: this wave's positions only (see moda_fwd.hpp) ----
-  if (wave_active && p.L_d > 0) {
+  if (wave_active && p.L_d > 0 && part != 0) {
     const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
     const long long nlo = (long long)tw_min * L_cap + slot_lo;
     const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
@@ -448,6 +499,58 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           o[dt] = mma16(tr_frag(reinterpret_cast<const char*>(vwave) + c * 16 * D * 2 + va[dt]), pf[c], o[dt]);
+    }
+  }
+
+  if constexpr (SPLIT) {
+    if (part >= 0) {
+      // this wave's state to the workspace; the second of the two waves
+      // (parts 0 and 1, same rows) to arrive merges and writes the output
+      //
+      // The two parts usually run on different XCDs, each with its own L2.
+      // A device-scope fence would write back and invalidate the whole L2 of
+      // the XCD (and with it the K/V blocks that its other workgroups still
+      // read), so the state goes through device-coherent accesses instead:
+      // relaxed device-scope atomic stores and loads (they bypass the stale
+      // L2 copies), and the counter.  The wait for every store to complete
+      // before the counter is incremented, and the second arrival's loads
+      // issued only after its increment has returned, order the two.
+      const int st = bh * p.nsplit + (p.ntiles - 1 - tile);
+      float* mine = p.ws + ((long long)(st * 2 + part) * NW + wave) * (kSplitState * 64) + lane;
+      float* other = p.ws + ((long long)(st * 2 + (part ^ 1)) * NW + wave) * (kSplitState * 64) + lane;
+      auto put = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      auto get = [](float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) put(mine + (dt * 16 + i) * 64, o[dt][i]);
+      put(mine + 64 * 64, m_run);
+      put(mine + 65 * 64, l_run);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store of the state has completed
+      uint32_t ticket = 0;
+      if (lane == 0)
+        ticket = __hip_atomic_fetch_add(p.cnt + st * NW + wave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ticket = __builtin_amdgcn_readfirstlane(ticket);
+      if (ticket == 0) return;                  // the other part merges
+      asm volatile("" ::: "memory");            // its state is read only now
+      // the merge is written in terms of part 0 and part 1 whichever of them
+      // arrives second (x = fma(s0, x0, s1 * x1)), so repeated calls agree
+      // bit for bit
+      const float m_o = get(other + 64 * 64), l_o = get(other + 65 * 64);
+      const float m_new = fmaxf(m_run, m_o);
+      const float a = __builtin_amdgcn_exp2f(m_run - m_new), c = __builtin_amdgcn_exp2f(m_o - m_new);
+      const bool p0 = part == 0;
+      const float s0 = p0 ? a : c, s1 = p0 ? c : a;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = o[dt][i], y = get(other + (dt * 16 + i) * 64);
+          o[dt][i] = __builtin_fmaf(s0, p0 ? x : y, s1 * (p0 ? y : x));
+        }
+      l_run = __builtin_fmaf(s0, p0 ? l_run : l_o, s1 * (p0 ? l_o : l_run));
+      m_run = m_new;
+      if (lane == 0) __hip_atomic_store(p.cnt + st * NW + wave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 

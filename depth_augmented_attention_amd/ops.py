@@ -111,13 +111,35 @@ def moda_append_depth(k_new: torch.Tensor, v_new: torch.Tensor, k_packed: torch.
 def moda_fwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
              k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-             with_lse: bool = True, stream=None):
+             with_lse: bool = True, stream=None, work: torch.Tensor | None = None):
     """MoDA forward.  q [B,T,Hq,d]; k_seq, v_seq [B,T,Hkv,d]; k_depth, v_depth
     are the packed buffers from moda_pack_depth (None when L_d == 0).
 
+    work: optional workspace from fwd_workspace(q, k_seq) -- the call then
+    goes to moda_fwd_ws, which splits the key range of the longest query
+    tiles on small grids (short sequences).
+
     Returns (out [B,T,Hq,d], lse [B,Hq,T] float32 or None).
     """
+    if work is not None:
+        return _fwd_call("moda_fwd_ws", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, with_lse,
+                         stream, work=work)
     return _fwd_call("moda_fwd", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, with_lse, stream)
+
+
+def fwd_workspace_bytes(B: int, T: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype) -> int:
+    n = load().moda_fwd_workspace_bytes(B, T, Hq, Hkv, d, _DT.get(dtype, -1))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def fwd_workspace(q: torch.Tensor, k_seq: torch.Tensor) -> torch.Tensor:
+    """A zero-filled workspace for moda_fwd(..., work=...) on these shapes
+    (uint8 on q's device; at least one byte so that it has an address)."""
+    B, T, Hq, d = q.shape
+    n = fwd_workspace_bytes(B, T, Hq, k_seq.shape[2], d, q.dtype)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
 def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
@@ -134,9 +156,10 @@ def moda_fwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                      with_lse, stream)
 
 
-def _fwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse, with_lse, stream):
-    """Checks and the call of moda_fwd (fn = "moda_fwd": L_cap slots, all
-    read) or moda_fwd_window (fn = "moda_fwd_window")."""
+def _fwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse, with_lse, stream,
+              work=None):
+    """Checks and the call of moda_fwd / moda_fwd_ws (L_cap slots, all read)
+    or moda_fwd_window."""
     if q.dim() != 4 or k_seq.dim() != 4 or v_seq.shape != k_seq.shape:
         raise ValueError("q must be [B,T,Hq,d], k_seq / v_seq [B,T,Hkv,d]")
     B, T, Hq, d = q.shape
@@ -169,11 +192,17 @@ def _fwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, ou
         if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
             raise ValueError("lse must be float32 [B,Hq,T]")
     dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse)
-    slots = (L_cap,) if fn == "moda_fwd" else (L_cap, slot_lo, slot_hi)
+    slots = (L_cap, slot_lo, slot_hi) if fn == "moda_fwd_window" else (L_cap,)
+    extra = ()
+    if fn == "moda_fwd_ws":
+        _dev(work, "work")
+        if work.device != q.device:
+            raise ValueError("work must be on q's device")
+        extra = (work.data_ptr(), work.numel() * work.element_size())
     st = _call(dev, fn, stream,
         q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
         out.data_ptr(), lse.data_ptr() if lse is not None else None,
-        B, T, Hq, Hkv, d, *slots, _dtype_code(q))
+        B, T, Hq, Hkv, d, *slots, _dtype_code(q), *extra)
     check(st, fn)
     return out, lse
 

@@ -59,7 +59,8 @@ typedef enum {
   MODA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent      */
   MODA_ERR_DTYPE = 3,       /* unknown dtype                                */
   MODA_ERR_UNSUPPORTED = 4, /* valid but not built (head size not 64/128)   */
-  MODA_ERR_HIP = 5          /* the HIP runtime reported an error on launch  */
+  MODA_ERR_HIP = 5,         /* the HIP runtime reported an error on launch  */
+  MODA_ERR_WORKSPACE = 6    /* workspace NULL, misaligned or too small      */
 } moda_status;
 
 /*
@@ -120,6 +121,55 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
              void* stream);
 
 /*
+ * moda_fwd_workspace_bytes -- size in bytes of the workspace that moda_fwd_ws
+ * uses for these sizes, or -1 for invalid sizes.  0 when every query tile runs
+ * whole anyway: grids of more than two workgroups per compute unit (about
+ * T * Hq / Hkv * B * Hkv > 65536 rows), shapes other than bf16 with d = 128.
+ * The size depends on B, T, G = Hq / Hkv and Hkv only: a 4096-byte header
+ * of arrival counters (the same for every shape), then 2 * 66 * 64 * 4 =
+ * 33792 bytes per (split tile, wave) for the two parts' states.  Splitting
+ * applies to grids of at most 512 workgroups (at most 1024 (split tile,
+ * wave) pairs), so it is at most 4096 + 1024 * 33792 bytes (33 MiB) for any
+ * shape.
+ */
+long long moda_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int dtype);
+
+/*
+ * moda_fwd_ws -- moda_fwd with a workspace, for short sequences.
+ *
+ * The causal mask gives the query tile at the end of the sequence about
+ * twice the keys of the average tile, and on a grid too small to fill the GPU
+ * more than twice over that tile alone sets the run time; the pages single out
+ * short sequences as the costly case for the depth slots (mhpn.cn article
+ * "动态混合深度注意力机制MoDA技术解析", section 3.1, Table 2 discussion: extra
+ * time 25.86% at 4K against 2.73% at 64K).  Here the key range of each of the
+ * longer half of the tiles is split over two workgroups whose partial
+ * softmax states (running max m, sum l, unnormalised output O) are merged
+ * exactly as one online softmax over the union of the two key sets -- the
+ * identity behind the Unified Softmax of gist.science (de) "Mixture-of-Depths
+ * Attention", Technische Zusammenfassung section 2.
+ *
+ *   q ... dtype, stream : as for moda_fwd
+ *   work       : device scratch owned by the caller, at least
+ *                moda_fwd_workspace_bytes(B, T, Hq, Hkv, d, dtype) bytes,
+ *                256-byte aligned.  Zero-fill it once before its first use;
+ *                every call leaves it ready for the next one (its arrival
+ *                counters return to zero).  Calls that share a workspace
+ *                must not run at the same time (same stream, or ordered by
+ *                events).
+ *   work_bytes : size of work in bytes
+ * Errors: MODA_ERR_WORKSPACE when work is NULL, not 256-byte aligned or too
+ * small (when the size needed is 0 any work pointer is accepted and unused);
+ * otherwise as for moda_fwd.  Results equal moda_fwd's within floating-point
+ * rounding (the merge reorders the sums of split tiles).
+ */
+int moda_fwd_ws(const void* q, const void* k_seq, const void* v_seq,
+                const void* k_depth, const void* v_depth,
+                void* out, float* lse,
+                int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+                void* work, long long work_bytes, void* stream);
+
+/*
  * moda_fwd_window -- fused forward over a window of depth slots.
  *
  * The depth stream can hold more slots than one layer reads: a buffer packed
@@ -132,8 +182,10 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
  *
  *   k_depth, v_depth : packed buffers with L_cap slots per position, i.e.
  *                      moda_depth_packed_elems(B, T, Hkv, d, L_cap) elements
- *                      each; every slot must hold finite values (zero-fill
- *                      a buffer before appending into it); NULL allowed iff
+ *                      each; slots outside the window and the padding rows
+ *                      are never read into a product, so they may hold
+ *                      anything (a buffer being filled by the write step
+ *                      needs no zero fill); NULL allowed iff
  *                      slot_lo == slot_hi
  *   L_cap            : slots per position in the packed buffers (>= 0)
  *   slot_lo, slot_hi : 0 <= slot_lo <= slot_hi <= L_cap

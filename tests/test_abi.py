@@ -216,3 +216,28 @@ def test_binding_rejects_mixed_devices():
     assert ops._one_device(a, None, a) == a.device
     with pytest.raises(ValueError):
         ops._one_device(a, torch.empty(0, device="meta"))
+
+
+def test_fwd_workspace_validation():
+    lib = _lib.load()
+    # small grids of the bf16 d = 128 kernel split their longest tiles: a
+    # 4096-byte counter header + two 66 x 64 float states per (split tile, wave)
+    units = 2 * 128 * 4                       # B = 1, T = 4096, G = 8, Hkv = 2: 128 split tiles per kv head
+    assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, 1) == 4096 + units * 33792
+    assert lib.moda_fwd_workspace_bytes(1, 1000, 8, 1, 128, 1) == 4096 + 31 * 4 * 33792
+    assert lib.moda_fwd_workspace_bytes(1, 65536, 16, 2, 128, 1) == 0     # big grid: whole tiles
+    assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, 0) == 0      # float32: generic kernel
+    assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 64, 1) == 0       # d = 64: generic kernel
+    assert lib.moda_fwd_workspace_bytes(1, 1, 2, 1, 128, 1) == 0          # one tile: nothing to split
+    assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 3, 128, 1) == -1     # Hq not a multiple of Hkv
+    # no shape needs more than 512 workgroups' worth
+    worst = max(lib.moda_fwd_workspace_bytes(B, T, Hq, 1, 128, 1)
+                for B in (1, 2, 4) for T in (64, 257, 1000, 4096, 8191) for Hq in (1, 8, 32, 64))
+    assert 0 < worst <= 4096 + 1024 * 33792
+    need = lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, 1)
+    a = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4096, 16, 2, 128, 24, 1)
+    assert lib.moda_fwd_ws(*a, None, need, None) == _lib.MODA_ERR_WORKSPACE               # no workspace
+    assert lib.moda_fwd_ws(*a, 4096, need - 1, None) == _lib.MODA_ERR_WORKSPACE           # too small
+    assert lib.moda_fwd_ws(*a, 4096 + 64, need, None) == _lib.MODA_ERR_WORKSPACE          # misaligned
+    assert lib.moda_fwd_ws(*a[:7], 1, 4096, 16, 3, 128, 24, 1, 4096, need, None) == _lib.MODA_ERR_SHAPE
+    assert "workspace" in _lib.status_string(_lib.MODA_ERR_WORKSPACE)
