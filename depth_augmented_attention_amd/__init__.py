@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     moda_append_depth,
     moda_append_depth_q8,
     moda_bwd,
+    moda_bwd_noalloc,
     moda_bwd_q8,
     moda_bwd_window,
     moda_bwd_window_q8,

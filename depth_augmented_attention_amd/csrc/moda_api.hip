@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "moda.h"
 #include "moda_bwd.hpp"
 #include "moda_fwd.hpp"
@@ -140,7 +142,8 @@ const char* moda_status_string(int status) {
     case MODA_ERR_UNSUPPORTED: return "MODA_ERR_UNSUPPORTED: head size must be 64 or 128";
     case MODA_ERR_HIP: return "MODA_ERR_HIP: the HIP runtime reported an error";
     case MODA_ERR_WORKSPACE:
-      return "MODA_ERR_WORKSPACE: the workspace is NULL, misaligned or smaller than moda_fwd_workspace_bytes";
+      return "MODA_ERR_WORKSPACE: the workspace is NULL, misaligned or too small (moda_fwd_workspace_bytes), "
+             "or the sizes need more than the static scratch of moda_bwd_noalloc (B * Hq * T > 4194304)";
     default: return "unknown moda_status";
   }
 }
@@ -348,19 +351,46 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
+// The backward's work buffer for callers that cannot allocate
+// (moda_bwd_noalloc): a file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never uses its name as an address: the
+// per-device address comes from hipGetSymbolAddress, taken once per device on
+// the first call there with that device current.
+constexpr long long kScratchFloats = 8LL << 20;                  // 32 MiB: B * Hq * T <= 4M rows
+static __device__ __align__(256) float scratch[kScratchFloats];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static float* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch, or an error status.
+static int device_scratch(float** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MODA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return MODA_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float*>(a);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MODA_OK;
+}
+
+// work == nullptr with use_scratch: the work buffer is the device's static
+// scratch (checked against its size after the other arguments).
 static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                     const void* v_depth, const float* k_scale, const float* v_scale, int q8,
                     const void* out, const float* lse, const void* dout, void* dq,
                     void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
                     int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
-                    void* stream) {
+                    void* stream, bool use_scratch = false) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
-  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || !work)
+  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || (!work && !use_scratch))
     return MODA_ERR_NULL;
   const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
@@ -373,6 +403,12 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   if (ntiles * BH > 0x7fffffffLL || (long long)T * BH > 0x7fffffffLL || rows > 0x7fffffffLL ||
       (long long)B * T * Hq > 0x7fffffffLL * 4)
     return MODA_ERR_SHAPE;
+
+  if (use_scratch) {
+    if (2LL * B * Hq * T > kScratchFloats) return MODA_ERR_WORKSPACE;
+    const int st = device_scratch(&work);
+    if (st != MODA_OK) return st;
+  }
 
   moda::BwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
@@ -410,6 +446,15 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   if (L_d < 0) return MODA_ERR_SHAPE;
   return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
                   dv_seq, dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
+}
+
+int moda_bwd_noalloc(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                     const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+                     void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, int B, int T, int Hq,
+                     int Hkv, int d, int L_d, int dtype, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
+                  dv_seq, dk_depth, dv_depth, nullptr, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream, true);
 }
 
 int moda_bwd_window(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,

@@ -225,6 +225,38 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
                      stream)
 
 
+def moda_bwd_noalloc(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
+                     k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
+                     out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                     grads: tuple, stream=None):
+    """moda_bwd through the C entry point that allocates nothing: the work
+    buffer is the library's static per-GPU scratch (B * Hq * T <= 4M).  The
+    five gradient tensors must be supplied (`grads`, as returned by moda_bwd);
+    calls on one GPU must not overlap in time."""
+    if grads is None:
+        raise ValueError("moda_bwd_noalloc needs the gradient tensors (grads)")
+    (B, T, Hq, Hkv, d, L), grads, _ = _bwd_common(q, k_seq, v_seq, 0, L_d, out, lse, dout, grads, False)
+    kd_ptr = vd_ptr = None
+    if L > 0:
+        if k_depth is None or v_depth is None:
+            raise ValueError("packed depth buffers are required when slots are read")
+        n = depth_packed_elems(B, T, Hkv, d, L_d)
+        for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):
+            _dev(t, name)
+            if t.numel() != n or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
+        kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
+    ptr = [g.data_ptr() if g is not None else None for g in grads]
+    dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
+                      dout, *grads[:3], *(grads[3:] if L > 0 else ()))
+    st = _call(dev, "moda_bwd_noalloc", stream,
+        q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+        ptr[3], ptr[4], B, T, Hq, Hkv, d, L_d, _dtype_code(q))
+    check(st, "moda_bwd_noalloc")
+    return grads
+
+
 def _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout, grads, work):
     """Shape / dtype / device checks shared by the backward calls; allocates
     the gradients and the work buffer when not given."""
@@ -257,6 +289,8 @@ def _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout, grads, work):
         if g is None or tuple(g.shape) != s or g.dtype != q.dtype:
             raise ValueError(f"gradient {i} must be {q.dtype} {s}")
         _dev(g, f"gradient {i}")
+    if work is False:          # the caller passes no work buffer (moda_bwd_noalloc)
+        return (B, T, Hq, Hkv, d, L_d), grads, None
     if work is None:
         work = torch.empty(2, B, Hq, T, dtype=torch.float32, device=q.device)
     _dev(work, "work")

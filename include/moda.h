@@ -60,7 +60,8 @@ typedef enum {
   MODA_ERR_DTYPE = 3,       /* unknown dtype                                */
   MODA_ERR_UNSUPPORTED = 4, /* valid but not built (head size not 64/128)   */
   MODA_ERR_HIP = 5,         /* the HIP runtime reported an error on launch  */
-  MODA_ERR_WORKSPACE = 6    /* workspace NULL, misaligned or too small      */
+  MODA_ERR_WORKSPACE = 6    /* workspace NULL, misaligned or too small, or
+                               sizes beyond moda_bwd_noalloc's scratch      */
 } moda_status;
 
 /*
@@ -293,6 +294,28 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq,
              float* work,
              int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
              void* stream);
+
+/*
+ * moda_bwd_noalloc -- moda_bwd without the work argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * training loops, harnesses that forbid hipMalloc).  The work buffer is
+ * instead a static device array inside the library, one per GPU, held until
+ * the process ends: 32 MiB, enough for B * Hq * T <= 4194304 (4M); larger
+ * sizes return MODA_ERR_WORKSPACE before anything is enqueued.  The call
+ * allocates nothing (no hipMalloc / hipFree); its first call on a GPU looks up
+ * that GPU's copy of the array.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (concurrent streams, or
+ * threads) race: order them, or use moda_bwd with a buffer each.  The array
+ * keeps the last call's -Delta and -lse * sqrt(d) (nothing needs clearing:
+ * each call writes all it reads).  Other arguments, results and errors as for
+ * moda_bwd; the results are bit for bit those of moda_bwd.
+ */
+int moda_bwd_noalloc(const void* q, const void* k_seq, const void* v_seq,
+                     const void* k_depth, const void* v_depth,
+                     const void* out, const float* lse, const void* dout,
+                     void* dq, void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth,
+                     int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+                     void* stream);
 
 /*
  * moda_bwd_window -- moda_bwd for the forward moda_fwd_window(..., L_cap,

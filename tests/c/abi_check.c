@@ -35,6 +35,9 @@ int main(void) {
   EXPECT(moda_fwd(F, F, F, NULL, F, F, NULL, 1, 4, 2, 1, 128, 3, MODA_BF16, NULL), MODA_ERR_NULL);
   EXPECT(moda_fwd_window(F, F, F, F, F, F, NULL, 1, 4, 2, 1, 128, 4, 0, 5, MODA_BF16, NULL), MODA_ERR_SHAPE);
   EXPECT(moda_append_depth(F, F, F, F, 1, 4, 1, 128, 3, 3, MODA_BF16, NULL), MODA_ERR_SHAPE);
+  EXPECT(moda_bwd_noalloc(F, F, F, NULL, NULL, F, (const float*)F, F, F, F, F, NULL, NULL, 1, 65537, 64, 1, 128,
+                          0, MODA_BF16, NULL),
+         MODA_ERR_WORKSPACE);
   EXPECT(moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_BF16) > 0, 1);
   EXPECT(moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_F32), 0);
   EXPECT(moda_fwd_ws(F, F, F, F, F, F, NULL, 1, 4096, 16, 2, 128, 24, MODA_BF16, NULL, 1 << 30, NULL),

@@ -241,3 +241,15 @@ def test_fwd_workspace_validation():
     assert lib.moda_fwd_ws(*a, 4096 + 64, need, None) == _lib.MODA_ERR_WORKSPACE          # misaligned
     assert lib.moda_fwd_ws(*a[:7], 1, 4096, 16, 3, 128, 24, 1, 4096, need, None) == _lib.MODA_ERR_SHAPE
     assert "workspace" in _lib.status_string(_lib.MODA_ERR_WORKSPACE)
+
+
+def test_bwd_noalloc_validation():
+    lib = _lib.load()
+    # B * Hq * T = 2^22 + 64 rows: beyond the 32 MiB static scratch, rejected
+    # before anything is enqueued (no GPU needed)
+    args = [FAKE] * 11 + [None, None]
+    assert lib.moda_bwd_noalloc(*args, 1, 65537, 64, 1, 128, 0, 1, None) == _lib.MODA_ERR_WORKSPACE
+    assert lib.moda_bwd_noalloc(*args, 1, 65536, 64, 1, 128, -1, 1, None) == _lib.MODA_ERR_SHAPE
+    assert lib.moda_bwd_noalloc(*([FAKE] * 10), None, None, None, 1, 64, 4, 1, 128, 0, 1, None) \
+        == _lib.MODA_ERR_NULL
+    assert lib.moda_bwd_noalloc(*args, 1, 64, 4, 1, 96, 0, 1, None) == _lib.MODA_ERR_UNSUPPORTED
