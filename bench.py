@@ -471,6 +471,20 @@ def main():
             Fs = useful_flops(sB, sT, sHq, sd, sL)
             sweep[ws["name"]] = {"fwd_ms": t_d, "fwd_ms_L0": t_0, "overhead_vs_L0": t_d / t_0 - 1.0,
                                  "fwd_tflops": Fs / (t_d * 1e-3) / 1e12, "reps": reps}
+            if moda.fwd_workspace_bytes(sB, sT, sHq, sHkv, sd, sq.dtype) > 0:
+                # the same workload through moda_fwd_ws (longest tiles' key
+                # ranges split over two workgroups)
+                wk = moda.fwd_workspace(sq, sk)
+                moda.moda_fwd(sq, sk, sv, skp, svp, sL, out=so, lse=sl, work=wk)
+                torch.cuda.synchronize()
+                tw, tw0 = timed_launches(
+                    [lambda: moda.moda_fwd(sq, sk, sv, skp, svp, sL, out=so, lse=sl, work=wk),
+                     lambda: moda.moda_fwd(sq, sk, sv, None, None, 0, out=so, lse=sl, work=wk)], reps)
+                t_w, t_w0 = sorted(tw)[reps // 2], sorted(tw0)[reps // 2]
+                sweep[ws["name"]].update({"ws_fwd_ms": t_w, "ws_fwd_ms_L0": t_w0,
+                                          "ws_fwd_tflops": Fs / (t_w * 1e-3) / 1e12,
+                                          "ws_overhead_vs_L0": t_w / t_w0 - 1.0})
+                del wk
             del sq, sk, sv, skd, svd, skp, svp, so, sl
         res["overhead_sweep"] = sweep
 

@@ -25,6 +25,16 @@ int fwd_waves(int dtype, int d, long long rows, long long BH) {
   return kWaves;
 }
 
+// Multiply-shift constants of moda::div_g for the divisor x >= 1:
+// magic = ceil(2^(31+s) / x), s = ceil(log2 x), shift = 31 + s.
+void div_magic(int x, uint32_t* magic, int* shift) {
+  int sh = 0;
+  while ((1LL << sh) < x) ++sh;
+  const unsigned long long num = 1ULL << (31 + sh);
+  *magic = (uint32_t)((num + (unsigned long long)x - 1) / (unsigned long long)x);
+  *shift = 31 + sh;
+}
+
 bool valid_dtype(int dtype) { return dtype == MODA_F32 || dtype == MODA_BF16; }
 bool supported_d(int d) { return d == 64 || d == 128; }
 
@@ -259,7 +269,7 @@ int moda_append_depth_q8(const void* k_new, const void* v_new, int8_t* k_q, int8
   moda::AppendQ8Params p{k_new, v_new, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_cap, slot,
                          padded_depth_keys(T, L_cap)};
   const long long rows = (long long)B * T * Hkv;
-  const long long rpb = 256 / (d / 8);
+  const long long rpb = 256 / (d / moda::kQ8Elems);
   const long long grid = (rows + rpb - 1) / rpb;
   if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -291,19 +301,25 @@ int moda_pack_depth_q8(const void* k_depth, const void* v_depth, int8_t* k_q, in
   if (!k_depth || !v_depth || !k_q || !v_q || !k_scale || !v_scale) return MODA_ERR_NULL;
   if ((long long)T * L_d > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;
   moda::PackQ8Params p{k_depth, v_depth, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
-  const long long rows = (long long)B * Hkv * p.NKp;
-  const long long rpb = 256 / (d / 8);
-  const long long grid = (rows + rpb - 1) / rpb;
-  if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  div_magic(L_d, &p.ld_magic, &p.ld_shift);
+  // (b, kv head) planes by blocks of rows; at most 65535 planes per launch
+  const long long rpb = 2 * (256 / (d / moda::kQ8Elems));     // two rows per lane group
+  const long long gx = (p.NKp + rpb - 1) / rpb;
+  const long long planes = (long long)B * Hkv;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == MODA_BF16) {
-    if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
-  } else {
-    if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 128>), dim3((unsigned)grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  for (long long bh0 = 0; bh0 < planes; bh0 += 65535) {
+    p.bh0 = (int)bh0;
+    const dim3 grid((unsigned)gx, (unsigned)(planes - bh0 < 65535 ? planes - bh0 : 65535));
+    if (dtype == MODA_BF16) {
+      if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 128>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 64>), grid, dim3(256), 0, s, p);
+    } else {
+      if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 128>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<float, 64>), grid, dim3(256), 0, s, p);
+    }
+    if (hipGetLastError() != hipSuccess) return MODA_ERR_HIP;
   }
-  return hipGetLastError() == hipSuccess ? MODA_OK : MODA_ERR_HIP;
+  return MODA_OK;
 }
 
 int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
@@ -422,13 +438,7 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.NKp = padded_depth_keys(T, L_cap);
   p.scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
-  {
-    int sh = 0;
-    while ((1LL << sh) < G) ++sh;                                 // ceil(log2 G)
-    const unsigned long long num = 1ULL << (31 + sh);
-    p.g_magic = (uint32_t)((num + (unsigned long long)G - 1) / (unsigned long long)G);
-    p.g_shift = 31 + sh;
-  }
+  div_magic(G, &p.g_magic, &p.g_shift);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

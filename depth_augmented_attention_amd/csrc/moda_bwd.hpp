@@ -74,13 +74,6 @@ struct BwdParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Quotient by the GQA group size through one 32x32->64-bit multiply (the
-// round-up reciprocal of Granlund and Montgomery, "Division by invariant
-// integers using multiplication", 1994): exact for 0 <= x < 2^31 with
-// magic = ceil(2^(31+s) / G), s = ceil(log2 G), shift = 31 + s.
-__device__ __forceinline__ int div_g(int x, uint32_t magic, int shift) {
-  return (int)(((uint64_t)(uint32_t)x * magic) >> shift);
-}
 
 // Four rows x VE elements (v[r] = VE consecutive elements of row row0 + r,
 // starting at element e0) written transposed: sT[(e0 + e) * LDT + row0 + r].

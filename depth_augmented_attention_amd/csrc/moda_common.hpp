@@ -108,6 +108,15 @@ template <> struct Dequant<float> {
   static __device__ __forceinline__ float one(int8_t c, float s) { return s * (float)c; }
 };
 
+// Quotient by a divisor fixed for the launch (the GQA group size, the depth
+// count) through one 32x32->64-bit multiply (the round-up reciprocal of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): exact for 0 <= x < 2^31 with
+// magic = ceil(2^(31+s) / G), s = ceil(log2 G), shift = 31 + s.
+__device__ __forceinline__ int div_g(int x, uint32_t magic, int shift) {
+  return (int)(((uint64_t)(uint32_t)x * magic) >> shift);
+}
+
 // Row order of the 32-key operand tiles.  A 32x32 accumulator gives lane half
 // h the rows {8q + 4h + i : q = 0..3, i = 0..3}; loading key pi(m) into operand
 // row m (pi swaps bits 2 and 3 of m) makes the 16 values a lane holds be the

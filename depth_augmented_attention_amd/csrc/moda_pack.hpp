@@ -103,8 +103,10 @@ namespace moda {
 // 8-bit depth KV (a memory tip of the mhpn.cn article, section 4.2): the same
 // packed rows as moda_pack_depth_kernel, each stored as d int8 codes plus one
 // float32 scale, scale = max|x| / 127 and code = rint(x / scale) clamped to
-// +-127 (0 for an all-zero row), every step in float32.  LPR lanes per packed
-// row, 8 elements each; the row maximum is reduced across those lanes.
+// +-127 (0 for an all-zero row), every step in float32.  D / 16 lanes per
+// packed row, 16 elements each; the row maximum is reduced across those
+// lanes.  A two-dimensional grid ((b, kv head) planes by row blocks) and a
+// multiply-shift quotient by L_d keep 64-bit divisions out of the index math.
 struct PackQ8Params {
   const void* kd;
   const void* vd;
@@ -114,54 +116,94 @@ struct PackQ8Params {
   float* vs;
   int B, T, Hkv, L_d;
   long long NKp;
+  uint32_t ld_magic;  // n / L_d == (n * ld_magic) >> ld_shift for 0 <= n < 2^31
+  int ld_shift;
+  int bh0;            // first (b, kv head) plane of this launch
 };
 
+constexpr int kQ8Elems = 16;   // elements per lane
+
 template <typename E>
-__device__ __forceinline__ void load8(const E* p, float (&v)[8]);
+__device__ __forceinline__ void load16(const E* p, float (&v)[kQ8Elems]);
 template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
-  const bf16x8 f = *reinterpret_cast<const bf16x8*>(p);
+__device__ __forceinline__ void load16<bf16>(const bf16* p, float (&v)[kQ8Elems]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (float)f[j];
+  for (int h = 0; h < 2; ++h) {
+    const bf16x8 f = *reinterpret_cast<const bf16x8*>(p + 8 * h);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[8 * h + j] = (float)f[j];
+  }
 }
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+__device__ __forceinline__ void load16<float>(const float* p, float (&v)[kQ8Elems]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { v[j] = a[j]; v[4 + j] = b[j]; }
+  for (int h = 0; h < 4; ++h) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * h + j] = a[j];
+  }
 }
 
-__device__ __forceinline__ u32x2 quantize8(const float (&x)[8], float scale) {
-  u32x2 w = {0u, 0u};
+// Codes rint(x / scale), clamped to +-127, of 16 elements; the quotient is
+// the correctly rounded float32 one.  It is formed as x * r first, with r the
+// hardware reciprocal of scale (within 1 ulp, 2^-23 relative): that product
+// is within 2^-22 relative (at most 3.1e-5 for |x / scale| <= 127) of the
+// exact quotient, and the correctly rounded quotient within 2^-24 relative
+// of it, so both round to the same integer unless one of them lies within
+// about 4e-5 of a half-integer.  A lane with a product within 1e-4 of a
+// half-integer (rare) divides exactly instead.  Same codes either way, at a
+// fraction of the cost of IEEE divisions.
+__device__ __forceinline__ u32x4 quantize16(const float (&x)[kQ8Elems], float scale) {
+  u32x4 w = {0u, 0u, 0u, 0u};
   if (scale > 0.f) {
+    const float r = __builtin_amdgcn_rcpf(scale);
+    float c[kQ8Elems];
+    bool near_tie = false;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float c = rintf(x[j] / scale);
-      c = fminf(fmaxf(c, -127.f), 127.f);
-      w[j >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (j & 3));
+    for (int j = 0; j < kQ8Elems; ++j) {
+      const float y = x[j] * r;
+      c[j] = rintf(y);
+      near_tie |= fabsf(y - c[j]) > 0.4999f;
+    }
+    if (near_tie) {
+#pragma unroll
+      for (int j = 0; j < kQ8Elems; ++j) c[j] = rintf(x[j] / scale);
+    }
+    // |x| <= max|x| and scale = max|x| / 127 rounded, so |x / scale| <=
+    // 127 (1 + 2^-24) and every code is already within +-127: the clamp is
+    // a no-op here.  Four codes go into one word by byte permutes (the low
+    // byte of each 32-bit integer).
+#pragma unroll
+    for (int q = 0; q < kQ8Elems / 4; ++q) {
+      const uint32_t i0 = (uint32_t)(int)c[4 * q], i1 = (uint32_t)(int)c[4 * q + 1];
+      const uint32_t i2 = (uint32_t)(int)c[4 * q + 2], i3 = (uint32_t)(int)c[4 * q + 3];
+      const uint32_t lo = __builtin_amdgcn_perm(i1, i0, 0x0c0c0400u);   // bytes: i0.b0, i1.b0, 0, 0
+      const uint32_t hi = __builtin_amdgcn_perm(i3, i2, 0x04000c0cu);   // bytes: 0, 0, i2.b0, i3.b0
+      w[q] = lo | hi;
     }
   }
   return w;
 }
 
-// Quantise one row of K and one row of V (D elements each) with LPR = D / 8
-// lanes per row, 8 elements per lane: the row maximum is reduced across the
+// Quantise one row of K and one row of V (D elements each) with D / 16
+// lanes per row, 16 elements per lane: the row maximum is reduced across the
 // row's lanes (every lane of the wave takes part in the exchange), then codes
-// and scales are written when `valid`.  Rows with valid == false but
+// and scales are written when `store`.  Rows with load == false but
 // store == true are padding: scale 0, codes 0.
 template <typename E, int D>
 __device__ __forceinline__ void quant_rows(const E* srck, const E* srcv, bool load, bool store, int l,
                                            int8_t* dk, int8_t* dv, float* sk_out, float* sv_out) {
-  constexpr int LPR = D / 8;
-  float xk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int LPR = D / kQ8Elems;
+  float xk[kQ8Elems], xv[kQ8Elems];
+#pragma unroll
+  for (int j = 0; j < kQ8Elems; ++j) { xk[j] = 0.f; xv[j] = 0.f; }
   if (load) {
-    load8(srck + l * 8, xk);
-    load8(srcv + l * 8, xv);
+    load16(srck + l * kQ8Elems, xk);
+    load16(srcv + l * kQ8Elems, xv);
   }
   float mk = 0.f, mv = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { mk = fmaxf(mk, fabsf(xk[j])); mv = fmaxf(mv, fabsf(xv[j])); }
+  for (int j = 0; j < kQ8Elems; ++j) { mk = fmaxf(mk, fabsf(xk[j])); mv = fmaxf(mv, fabsf(xv[j])); }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) {
     mk = fmaxf(mk, __shfl_xor(mk, off));
@@ -169,8 +211,8 @@ __device__ __forceinline__ void quant_rows(const E* srck, const E* srcv, bool lo
   }
   const float sk = mk / 127.f, sv = mv / 127.f;
   if (store) {
-    *reinterpret_cast<u32x2*>(dk + l * 8) = quantize8(xk, sk);
-    *reinterpret_cast<u32x2*>(dv + l * 8) = quantize8(xv, sv);
+    *reinterpret_cast<u32x4*>(dk + l * kQ8Elems) = quantize16(xk, sk);
+    *reinterpret_cast<u32x4*>(dv + l * kQ8Elems) = quantize16(xv, sv);
     if (l == 0) {
       *sk_out = sk;
       *sv_out = sv;
@@ -178,28 +220,52 @@ __device__ __forceinline__ void quant_rows(const E* srck, const E* srcv, bool lo
   }
 }
 
+// Two packed rows per lane group, their loads issued together (more loads in
+// flight per thread).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p) {
-  constexpr int LPR = D / 8;                    // lanes per packed row
-  constexpr int RPB = 256 / LPR;                // rows per workgroup
-  const long long rows = (long long)p.B * p.Hkv * p.NKp;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  constexpr int LPR = D / kQ8Elems;             // lanes per packed row
+  constexpr int RPB = 256 / LPR;                // rows per workgroup and pass
+  const int bh = p.bh0 + (int)blockIdx.y;       // (b, kv head) plane
   const int l = threadIdx.x % LPR;
-  bool load = false;
-  long long src = 0;
-  if (row < rows) {
-    const long long bh = row / p.NKp;
-    const int n = (int)(row % p.NKp);
-    if (n < p.T * p.L_d) {
-      const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
-      const int t = n / p.L_d, j = n - t * p.L_d;
-      src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D;
-      load = true;
+  const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
+  float xk[2][kQ8Elems], xv[2][kQ8Elems];
+  bool in_plane[2];
+  long long dst[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int n = ((int)blockIdx.x * 2 + u) * RPB + (int)threadIdx.x / LPR;   // packed row in the plane
+    in_plane[u] = n < p.NKp;
+    dst[u] = (long long)bh * p.NKp + (in_plane[u] ? n : 0);
+#pragma unroll
+    for (int j = 0; j < kQ8Elems; ++j) { xk[u][j] = 0.f; xv[u][j] = 0.f; }
+    if (in_plane[u] && n < p.T * p.L_d) {
+      const int t = div_g(n, p.ld_magic, p.ld_shift), jj = n - t * p.L_d;
+      const long long src = ((((long long)b * p.T + t) * p.L_d + jj) * p.Hkv + kvh) * D + l * kQ8Elems;
+      load16(reinterpret_cast<const E*>(p.kd) + src, xk[u]);
+      load16(reinterpret_cast<const E*>(p.vd) + src, xv[u]);
     }
   }
-  const long long r = row < rows ? row : 0;
-  quant_rows<E, D>(reinterpret_cast<const E*>(p.kd) + src, reinterpret_cast<const E*>(p.vd) + src, load,
-                   row < rows, l, p.kq + r * D, p.vq + r * D, p.ks + r, p.vs + r);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float mk = 0.f, mv = 0.f;
+#pragma unroll
+    for (int j = 0; j < kQ8Elems; ++j) { mk = fmaxf(mk, fabsf(xk[u][j])); mv = fmaxf(mv, fabsf(xv[u][j])); }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) {
+      mk = fmaxf(mk, __shfl_xor(mk, off));
+      mv = fmaxf(mv, __shfl_xor(mv, off));
+    }
+    const float sk = mk / 127.f, sv = mv / 127.f;
+    if (in_plane[u]) {
+      *reinterpret_cast<u32x4*>(p.kq + dst[u] * D + l * kQ8Elems) = quantize16(xk[u], sk);
+      *reinterpret_cast<u32x4*>(p.vq + dst[u] * D + l * kQ8Elems) = quantize16(xv[u], sv);
+      if (l == 0) {
+        p.ks[dst[u]] = sk;
+        p.vs[dst[u]] = sv;
+      }
+    }
+  }
 }
 
 // Write step with 8-bit depth KV: one layer's K/V rows quantised into slot
@@ -218,7 +284,7 @@ struct AppendQ8Params {
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void moda_append_depth_q8_kernel(AppendQ8Params p) {
-  constexpr int LPR = D / 8;
+  constexpr int LPR = D / kQ8Elems;
   constexpr int RPB = 256 / LPR;
   const long long rows = (long long)p.B * p.T * p.Hkv;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, t, kvh) in input order

@@ -66,6 +66,36 @@ def test_pack_q8_bitwise(case):
     assert np.array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_pack_q8_ties_and_near_ties(dtype):
+    """Rows whose quotients x / scale land exactly on half-integers (scale 1:
+    row maximum 127) and rows with quotients a few ulps either side of
+    half-integers: codes bit for bit the oracle's (ties to even), which takes
+    the kernel's exact-division path."""
+    _say(f"q8 ties {dtype}")
+    B, T, L, Hkv, d = 1, 40, 3, 2, 128
+    g = torch.Generator().manual_seed(17)
+    x = torch.randn(B, T, L, Hkv, d, generator=g, dtype=torch.float32)
+    halves = torch.arange(-64, 64, dtype=torch.float32) + 0.5            # -63.5 .. 63.5
+    x[0, :10, :, :, :] = halves                                           # exact ties after max = 127
+    x[0, :10, :, :, 0] = 127.0
+    # quotients just off the half-integers: scale = 127 / 127 * s for s = 1 + 2^-k
+    for k, t in zip(range(6, 16), range(10, 20)):
+        sc = 1.0 + 2.0 ** -k
+        x[0, t, :, :, :] = (halves + 2.0 ** -k) * sc
+        x[0, t, :, :, 0] = 127.0 * sc
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    kd, vd = x, x.flip(-1).contiguous()
+    kq, vq, ks, vs = moda.moda_pack_depth_q8(kd.cuda(), vd.cuda())
+    torch.cuda.synchronize()
+    rkq, rks, rvq, rvs = _ref_q8(kd, vd)
+    assert np.array_equal(kq.cpu().numpy(), rkq)
+    assert np.array_equal(vq.cpu().numpy(), rvq)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+
+
 def _deq_logical(kd):
     """Oracle dequantised depth tensor in the logical layout (float64)."""
     codes, scales = quantize_rows(np32(kd))
