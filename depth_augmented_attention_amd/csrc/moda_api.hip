@@ -1,6 +1,7 @@
 // C ABI of libmoda.so (declared in include/moda.h): argument validation,
 // kernel selection and launch on the caller's stream.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 
 #include <mutex>
@@ -13,6 +14,18 @@
 
 namespace {
 
+// Products of sizes (all >= 0), saturated at LLONG_MAX instead of
+// overflowing: validation compares them with limits, so a saturated product
+// is rejected like any other too-large one.
+long long smul(long long a, long long b) {
+  if (a == 0 || b == 0) return 0;
+  return a > LLONG_MAX / b ? LLONG_MAX : a * b;
+}
+long long smul(long long a, long long b, long long c) { return smul(smul(a, b), c); }
+long long smul(long long a, long long b, long long c, long long e) { return smul(smul(a, b, c), e); }
+// ceil(x / y) for x >= 0, y > 0, without overflow
+long long cdiv(long long x, long long y) { return x / y + (x % y != 0); }
+
 constexpr int kWaves = 4;          // waves per workgroup of the forward kernels
 
 // Waves per workgroup of the forward for (dtype, d, shape): the bf16 d = 128
@@ -21,7 +34,7 @@ constexpr int kWaves = 4;          // waves per workgroup of the forward kernels
 // generic kernel.
 constexpr long long kCUs = 256;     // compute units of an MI355X
 int fwd_waves(int dtype, int d, long long rows, long long BH) {
-  if (dtype == MODA_BF16 && d == 128 && (rows + 255) / 256 * BH >= 2 * kCUs) return 8;
+  if (dtype == MODA_BF16 && d == 128 && smul((rows + 255) / 256, BH) >= 2 * kCUs) return 8;
   return kWaves;
 }
 
@@ -62,7 +75,7 @@ SplitPlan split_plan(int dtype, int d, long long rows, long long BH) {
   SplitPlan sp;
   if (fwd_waves(dtype, d, rows, BH) != 4 || dtype != MODA_BF16 || d != 128) return sp;
   const long long ntiles = (rows + 127) / 128;
-  if (ntiles * BH > 2 * kCUs || ntiles < 2) return sp;
+  if (smul(ntiles, BH) > 2 * kCUs || ntiles < 2) return sp;
   sp.nsplit = (int)(ntiles / 2);
   const long long units = BH * sp.nsplit * 4;    // (split tile, wave) pairs, <= kSplitCntBytes / 4
   sp.cnt_bytes = kSplitCntBytes;
@@ -160,7 +173,9 @@ const char* moda_status_string(int status) {
 
 long long moda_depth_packed_elems(int B, int T, int Hkv, int d, int L_d) {
   if (B < 1 || T < 1 || Hkv < 1 || d < 1 || L_d < 0) return -1;
-  return (long long)B * Hkv * padded_depth_keys(T, L_d) * d;
+  if ((long long)T * L_d > 0x7fffffffLL - 32) return -1;           // packed key index is 31-bit
+  const long long n = smul(B, Hkv, padded_depth_keys(T, L_d), d);
+  return n == LLONG_MAX ? -1 : n;
 }
 
 int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, void* v_packed,
@@ -173,7 +188,7 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   if ((long long)T * L_d > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;
   moda::PackParams p{k_depth, v_depth, k_packed, v_packed, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
   const int ve = dtype == MODA_BF16 ? 8 : 4;
-  const long long grid = ((long long)B * Hkv * p.NKp * (d / ve) + 255) / 256;
+  const long long grid = cdiv(smul(B, Hkv, p.NKp, d / ve), 256);
   if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -203,7 +218,7 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   const int nw = fwd_waves(dtype, d, rows, (long long)B * Hkv);
   const int tile_rows = 32 * nw;
   const long long ntiles = (rows + tile_rows - 1) / tile_rows;
-  const long long grid = ntiles * B * Hkv;
+  const long long grid = smul(ntiles, B, Hkv);
   if (grid > 0x7fffffffLL || rows > 0x7fffffffLL) return MODA_ERR_SHAPE;
 
   moda::FwdParams p;
@@ -268,9 +283,9 @@ int moda_append_depth_q8(const void* k_new, const void* v_new, int8_t* k_q, int8
   if (!k_new || !v_new || !k_q || !v_q || !k_scale || !v_scale) return MODA_ERR_NULL;
   moda::AppendQ8Params p{k_new, v_new, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_cap, slot,
                          padded_depth_keys(T, L_cap)};
-  const long long rows = (long long)B * T * Hkv;
+  const long long rows = smul(B, T, Hkv);
   const long long rpb = 256 / (d / moda::kQ8Elems);
-  const long long grid = (rows + rpb - 1) / rpb;
+  const long long grid = cdiv(rows, rpb);
   if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == MODA_BF16) {
@@ -333,6 +348,7 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
 long long moda_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int dtype) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv != 0) return -1;
   if (!valid_dtype(dtype)) return -1;
+  if (!supported_d(d)) return 0;
   return split_plan(dtype, d, (long long)T * (Hq / Hkv), (long long)B * Hkv).bytes;
 }
 
@@ -355,8 +371,8 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
   if (!k_new || !v_new || !k_packed || !v_packed) return MODA_ERR_NULL;
   moda::AppendParams p{k_new, v_new, k_packed, v_packed, B, T, Hkv, L_cap, slot, padded_depth_keys(T, L_cap)};
   const int ve = dtype == MODA_BF16 ? 8 : 4;
-  const long long threads = (long long)B * T * Hkv * (d / ve);
-  const long long grid = (threads + 255) / 256;
+  const long long threads = smul(B, T, Hkv, d / ve);
+  const long long grid = cdiv(threads, 256);
   if (grid > 0x7fffffffLL) return MODA_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -416,8 +432,8 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   const long long ntiles = (rows + 32 * kWaves - 1) / (32 * kWaves);
   const long long nktiles = ((long long)T + 32 * kWaves - 1) / (32 * kWaves);
   const long long BH = (long long)B * Hkv;
-  if (ntiles * BH > 0x7fffffffLL || (long long)T * BH > 0x7fffffffLL || rows > 0x7fffffffLL ||
-      (long long)B * T * Hq > 0x7fffffffLL * 4)
+  if (smul(ntiles, BH) > 0x7fffffffLL || smul(T, BH) > 0x7fffffffLL || rows > 0x7fffffffLL ||
+      smul(B, T, Hq) > 0x7fffffffLL * 4)
     return MODA_ERR_SHAPE;
 
   if (use_scratch) {
