@@ -555,17 +555,23 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // The output address is formed anew here rather than kept from the Q load
+  // through the sweep (a 64-bit value the register allocator would otherwise
+  // park in scratch), and the lane half comes from the lane count.
+  int t_out = t_row, h_out = hq;
+  asm volatile("" : "+v"(t_out), "+v"(h_out));
+  const int hh_out = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
   if (row_ok) {
     const float inv = 1.f / l_tot;
-    bf16* op = reinterpret_cast<bf16*>(p.out) + (((long long)b * T + t_row) * p.Hq + hq) * D;
+    bf16* op = reinterpret_cast<bf16*>(p.out) + (((long long)b * T + t_out) * p.Hq + h_out) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        store4(op + dt * 32 + g4 * 8 + hh * 4, o[dt][g4 * 4 + 0] * inv, o[dt][g4 * 4 + 1] * inv,
+        store4(op + dt * 32 + g4 * 8 + hh_out * 4, o[dt][g4 * 4 + 0] * inv, o[dt][g4 * 4 + 1] * inv,
                o[dt][g4 * 4 + 2] * inv, o[dt][g4 * 4 + 3] * inv);
-    if (hh == 0 && p.lse)
-      p.lse[((long long)b * p.Hq + hq) * T + t_row] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+    if (hh_out == 0 && p.lse)
+      p.lse[((long long)b * p.Hq + h_out) * T + t_out] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
