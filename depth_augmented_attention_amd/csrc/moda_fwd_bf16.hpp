@@ -220,15 +220,13 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   };
   // load spans [s_lo, s_hi) of block blk; slot i covers span i*NW + wave, which
   // lands at span (i*NW + wave - sp0) of lbase
-  auto dma_rows = [&](const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase, int s_lo, int s_hi,
-                      int sp0) {
+  auto dma_rows = [&]<int S_LO, int S_HI>(const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase) {
+    static_assert(S_LO % NW == 0 && S_HI % NW == 0, "span ranges are whole rounds of the waves");
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int sp = i * NW + wave;
-      if (sp >= s_lo && sp < s_hi) dma16(rs, off[i], lbase + (sp - sp0) * 512);
-    }
+    for (int i = S_LO / NW; i < S_HI / NW; ++i) dma16(rs, off[i], lbase + (i * NW + wave - S_LO) * 512);
   };
+
   const int klast = jhi - 1;
   auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
   // K stage st, half h (rows 32h .. 32h+31 of the block)
@@ -344,10 +342,10 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const bool sweep = jlo < jhi;                     // workgroup-uniform
   float s_a[16], s_b[16];
   if (sweep) {
-    dma_rows(kbase, jlo, offk, khalf(0, 0), 0, 8, 0);
-    dma_rows(kbase, jlo, offk, khalf(0, 1), 8, 16, 8);
-    dma_rows(kbase, clampb(jlo + 1), offk, khalf(1, 0), 0, 8, 0);
-    dma_rows(vbase, jlo, offv, vst(0), 0, 16, 0);
+    dma_rows.template operator()<0, 8>(kbase, jlo, offk, khalf(0, 0));
+    dma_rows.template operator()<8, 16>(kbase, jlo, offk, khalf(0, 1));
+    dma_rows.template operator()<0, 8>(kbase, clampb(jlo + 1), offk, khalf(1, 0));
+    dma_rows.template operator()<0, 16>(vbase, jlo, offv, vst(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     qk.template operator()<0, 0>(s_a);
@@ -361,9 +359,9 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   //   half 0: s_b = QK(K(j) rows 32-63) while softmax(s_a); P.V with V(j) rows 0-31
   //   half 1: s_a = QK(K(j+1) rows 0-31) while softmax(s_b); P.V with V(j) rows 32-63
   auto block = [&]<bool MASKED, int ST>(int j) {
-    dma_rows(kbase, clampb(j + 2), offk, khalf(ST, 0), 0, 8, 0);
-    dma_rows(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1), 8, 16, 8);
-    dma_rows(vbase, clampb(j + 1), offv, vst(ST ^ 1), 0, 16, 0);
+    dma_rows.template operator()<0, 8>(kbase, clampb(j + 2), offk, khalf(ST, 0));
+    dma_rows.template operator()<8, 16>(kbase, clampb(j + 1), offk, khalf(ST ^ 1, 1));
+    dma_rows.template operator()<0, 16>(vbase, clampb(j + 1), offv, vst(ST ^ 1));
     bf16x8 pf[2], vf[2 * NDT];
     float alpha;
     bool need;
