@@ -150,24 +150,28 @@ __device__ __forceinline__ void load16<float>(const float* p, float (&v)[kQ8Elem
 // is within 2^-22 relative (at most 3.1e-5 for |x / scale| <= 127) of the
 // exact quotient, and the correctly rounded quotient within 2^-24 relative
 // of it, so both round to the same integer unless one of them lies within
-// about 4e-5 of a half-integer.  A lane with a product within 1e-4 of a
-// half-integer (rare) divides exactly instead.  Same codes either way, at a
+// about 4e-5 of a half-integer.  An element whose product lies within 1e-4
+// of a half-integer (rare) is divided exactly instead, on its own: the other
+// elements of the lane keep their codes.  Same codes either way, at a
 // fraction of the cost of IEEE divisions.
 __device__ __forceinline__ u32x4 quantize16(const float (&x)[kQ8Elems], float scale) {
   u32x4 w = {0u, 0u, 0u, 0u};
   if (scale > 0.f) {
     const float r = __builtin_amdgcn_rcpf(scale);
-    float c[kQ8Elems];
-    bool near_tie = false;
+    float c[kQ8Elems], y[kQ8Elems];
+    float dev = 0.f;   // the lane's largest distance from an integer
 #pragma unroll
     for (int j = 0; j < kQ8Elems; ++j) {
-      const float y = x[j] * r;
-      c[j] = rintf(y);
-      near_tie |= fabsf(y - c[j]) > 0.4999f;
+      y[j] = x[j] * r;
+      c[j] = rintf(y[j]);
+      dev = fmaxf(dev, fabsf(y[j] - c[j]));
     }
-    if (near_tie) {
+    if (__builtin_expect(dev > 0.4999f, 0)) {
+      // only the elements near a half-integer divide exactly; an element
+      // that no lane of the wave needs is skipped
 #pragma unroll
-      for (int j = 0; j < kQ8Elems; ++j) c[j] = rintf(x[j] / scale);
+      for (int j = 0; j < kQ8Elems; ++j)
+        if (fabsf(y[j] - c[j]) > 0.4999f) c[j] = rintf(x[j] / scale);
     }
     // |x| <= max|x| and scale = max|x| / 127 rounded, so |x / scale| <=
     // 127 (1 + 2^-24) and every code is already within +-127: the clamp is
