@@ -403,17 +403,20 @@ def main():
         packed = moda.moda_pack_depth_q8(kd, vd)
         moda.moda_fwd_q8(q, ks, vs, packed, L_d, out=out, lse=lse)
         torch.cuda.synchronize()
-        eq = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-        for i in range(3):
-            eq[i].record()
-            moda.moda_pack_depth_q8(kd, vd)
-        eq[3].record()
+        # repack into the same buffers: median of 10 calls, each timed alone
+        ep = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a_, b_ in ep:
+            a_.record()
+            moda.moda_pack_depth_q8(kd, vd, out=packed)
+            b_.record()
+        eq = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        eq[0].record()
         for i in range(3):
             moda.moda_fwd_q8(q, ks, vs, packed, L_d, out=out, lse=lse)
-            eq[4 + i].record()
+            eq[1 + i].record()
         torch.cuda.synchronize()
-        q8_pack_ms = eq[0].elapsed_time(eq[3]) / 3
-        q8_fwd_ms = eq[3].elapsed_time(eq[6]) / 3
+        q8_pack_ms = med([a_.elapsed_time(b_) for a_, b_ in ep])
+        q8_fwd_ms = eq[0].elapsed_time(eq[3]) / 3
         depth_elems = kd.numel()
         q8_bytes = 2 * depth_elems + 2 * 4 * (depth_elems // d)       # codes + row scales, K and V
         res["q8_depth_bytes"] = q8_bytes

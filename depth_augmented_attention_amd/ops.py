@@ -371,18 +371,25 @@ def moda_bwd_q8(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor, packe
                               grads=grads, work=work, stream=stream)
 
 
-def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None):
+def moda_pack_depth_q8(k_depth: torch.Tensor, v_depth: torch.Tensor, stream=None, out=None):
     """8-bit packed depth KV: returns (k_q, v_q int8 flat buffers of
-    depth_packed_elems(...) codes, k_scale, v_scale float32 [elems / d])."""
+    depth_packed_elems(...) codes, k_scale, v_scale float32 [elems / d]),
+    written into `out` (such a tuple) when it is given."""
     if k_depth.dim() != 5 or v_depth.shape != k_depth.shape or v_depth.dtype != k_depth.dtype:
         raise ValueError("k_depth / v_depth must both be [B,T,L_d,Hkv,d] of one dtype")
     B, T, L_d, Hkv, d = k_depth.shape
     n = depth_packed_elems(B, T, Hkv, d, L_d)
     dev = k_depth.device
-    kq = torch.empty(n, dtype=torch.int8, device=dev)
-    vq = torch.empty(n, dtype=torch.int8, device=dev)
-    ks = torch.empty(n // d, dtype=torch.float32, device=dev)
-    vs = torch.empty(n // d, dtype=torch.float32, device=dev)
+    if out is not None:
+        if len(out) != 4:
+            raise ValueError("out must be (k_q, v_q, k_scale, v_scale)")
+        _check_q8(out, B, T, Hkv, d, L_d)
+        kq, vq, ks, vs = out
+    else:
+        kq = torch.empty(n, dtype=torch.int8, device=dev)
+        vq = torch.empty(n, dtype=torch.int8, device=dev)
+        ks = torch.empty(n // d, dtype=torch.float32, device=dev)
+        vs = torch.empty(n // d, dtype=torch.float32, device=dev)
     if L_d == 0:
         return kq, vq, ks, vs
     for t, name in ((k_depth, "k_depth"), (v_depth, "v_depth")):

@@ -64,6 +64,13 @@ def test_pack_q8_bitwise(case):
     assert np.array_equal(vq.cpu().numpy(), rvq)
     assert np.array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
     assert np.array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+    # the same codes written into caller buffers that held other bytes
+    out = tuple(torch.full_like(t, 7) for t in (kq, vq, ks, vs))
+    got = moda.moda_pack_depth_q8(kd.cuda(), vd.cuda(), out=out)
+    torch.cuda.synchronize()
+    assert all(g is o for g, o in zip(got, out))
+    for a, b in zip(out, (kq, vq, ks, vs)):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
