@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void moda_bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 31;
   const int hh = lane >> 5;
 
@@ -1047,7 +1047,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 31;
   const int hh = lane >> 5;
 
@@ -1143,10 +1143,19 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
           dp = mma16(va[kc], df[kc], dp);
         }
         bf16x8 dsf[2];
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], sl2, -lse2);
+        // the causal mask only where some key of the half lies past some row
+        // of the wave (a wave-uniform branch)
+        if (j * BN + H * 32 + 31 > tw_min) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            x[r] = j * BN + H * 32 + reg_key(r, hh) <= t_row ? x[r] : -INFINITY;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * BN + H * 32 + reg_key(r, hh);
-          const float pr = __builtin_amdgcn_exp2f(key <= t_row ? __builtin_fmaf(s[r], sl2, -lse2) : -INFINITY);
+          const float pr = __builtin_amdgcn_exp2f(x[r]);
           dsf[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dlt));
         }
 #pragma unroll
