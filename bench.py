@@ -53,13 +53,37 @@ def compulsory_bytes(w):
 FWD_SOURCES = ("moda_common.hpp", "moda_fwd.hpp", "moda_fwd_bf16.hpp")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank space, so that an edit of a
+    comment does not count as a change of the kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':                      # string literal, kept whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """Hash of the sources the fused forward kernel is compiled from."""
+    """Hash of the code (comments and spacing aside) of the sources the fused
+    forward kernel is compiled from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "depth_augmented_attention_amd", "csrc")
     for f in FWD_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

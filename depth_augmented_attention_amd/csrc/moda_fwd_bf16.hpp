@@ -218,8 +218,11 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         (void*)(reinterpret_cast<const char*>(head) + (long long)blk * BN * row_bytes), (short)0, bytes,
         kBufferWord3);
   };
-  // load spans [s_lo, s_hi) of block blk; slot i covers span i*NW + wave, which
-  // lands at span (i*NW + wave - sp0) of lbase
+  // load spans [S_LO, S_HI) of block blk: slot i covers span i*NW + wave,
+  // which lands at span (i*NW + wave - S_LO) of lbase.  The range is a whole
+  // number of rounds of the waves, so the slots a wave loads are known at
+  // compile time (no branch per load: fewer basic blocks in the sweep for
+  // the scheduler to work across)
   auto dma_rows = [&]<int S_LO, int S_HI>(const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase) {
     static_assert(S_LO % NW == 0 && S_HI % NW == 0, "span ranges are whole rounds of the waves");
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
