@@ -38,6 +38,7 @@ int fwd_waves(int dtype, int d, long long rows, long long BH) {
   return kWaves;
 }
 
+
 // Multiply-shift constants of moda::div_g for the divisor x >= 1:
 // magic = ceil(2^(31+s) / x), s = ceil(log2 x), shift = 31 + s.
 void div_magic(int x, uint32_t* magic, int* shift) {
@@ -66,6 +67,16 @@ long long padded_depth_keys(int T, int L_d) {
 // used the same workspace before; then the partial states of both parts of
 // every wave.
 constexpr long long kSplitCntBytes = 2 * kCUs / 2 * 4 * 4;
+// Grids of the bf16 d = 128 kernel that fit in one round of one eight-wave
+// workgroup per compute unit over 128-row tiles: the key-split layout, whose
+// two sets of four waves split each tile's key blocks (and depth tiles).
+// With a second round the two rounds' depth folds come one after the other,
+// and at T = 4K, G = 8, Hkv = 2 that costs more than the split saves.
+bool fwd_key_split(int dtype, int d, long long rows, long long BH) {
+  return dtype == MODA_BF16 && d == 128 && fwd_waves(dtype, d, rows, BH) == 4 &&
+         smul((rows + 127) / 128, BH) <= kCUs && rows > 128;
+}
+
 struct SplitPlan {
   int nsplit = 0;          // split tiles per (b, kv head)
   long long cnt_bytes = 0; // counter header
@@ -74,6 +85,7 @@ struct SplitPlan {
 SplitPlan split_plan(int dtype, int d, long long rows, long long BH) {
   SplitPlan sp;
   if (fwd_waves(dtype, d, rows, BH) != 4 || dtype != MODA_BF16 || d != 128) return sp;
+  if (fwd_key_split(dtype, d, rows, BH)) return sp;   // split inside the workgroup instead
   const long long ntiles = (rows + 127) / 128;
   if (smul(ntiles, BH) > 2 * kCUs || ntiles < 2) return sp;
   sp.nsplit = (int)(ntiles / 2);
@@ -88,6 +100,8 @@ hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, int nw, hipStream
   if constexpr (sizeof(E) == 2 && D == 128) {
     if (p.nsplit > 0)
       hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 4, true>), dim3(grid), dim3(4 * 64), 0, s, p);
+    else if (nw == -8)
+      hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 8, false, true>), dim3(grid), dim3(8 * 64), 0, s, p);
     else if (nw == 8)
       hipLaunchKernelGGL((moda::moda_fwd_bf16_kernel<D, 8>), dim3(grid), dim3(8 * 64), 0, s, p);
     else
@@ -215,8 +229,9 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   if (L_d > 0 && q8 && (!k_scale || !v_scale)) return MODA_ERR_NULL;
   const int G = Hq / Hkv;
   const long long rows = (long long)T * G;
-  const int nw = fwd_waves(dtype, d, rows, (long long)B * Hkv);
-  const int tile_rows = 32 * nw;
+  int nw = fwd_waves(dtype, d, rows, (long long)B * Hkv);
+  const bool ks = fwd_key_split(dtype, d, rows, (long long)B * Hkv);
+  const int tile_rows = 32 * nw;   // 128 for the key-split layout too
   const long long ntiles = (rows + tile_rows - 1) / tile_rows;
   const long long grid = smul(ntiles, B, Hkv);
   if (grid > 0x7fffffffLL || rows > 0x7fffffffLL) return MODA_ERR_SHAPE;
@@ -230,7 +245,7 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.ntiles = (int)ntiles;
   // at most two workgroups per compute unit for the whole grid: pair long
   // tiles with short ones (with more rounds, longest first balances by itself)
-  p.paired = grid <= 2 * kCUs && B * Hkv <= kCUs && kCUs % (B * Hkv) == 0;
+  p.paired = !ks && grid <= 2 * kCUs && B * Hkv <= kCUs && kCUs % (B * Hkv) == 0;
   p.NKp = padded_depth_keys(T, L_cap);
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.nsplit = 0;
@@ -247,6 +262,7 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
       launch_grid = (ntiles + sp.nsplit) * B * Hkv;
     }
   }
+  if (ks && p.nsplit == 0) nw = -8;   // (launch_fwd: the key-split instantiation)
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

@@ -96,35 +96,44 @@ constexpr int kSplitState = 66;
 
 // NW waves per workgroup (32 query rows each): 8, or 4 for small grids;
 // SPLIT: key ranges of the longest tiles split over two workgroups.
-template <int D, int NW, bool SPLIT = false>
+// KS (eight waves, small grids): the two sets of four waves share one
+// 128-row tile and split its key blocks and its depth tiles between them,
+// each set with its own LDS stages, and meet through LDS at the end -- one
+// workgroup per compute unit that sweeps a long tile's keys twice as fast.
+template <int D, int NW, bool SPLIT = false, bool KS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moda_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 128, "the bf16 fast path is built for head size 128");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(!KS || (NW == 8 && !SPLIT), "the key split is an eight-wave layout");
+  constexpr int NR = KS ? 4 : NW;         // 32-row groups of a tile
+  constexpr int NS = KS ? 2 : 1;          // sets of LDS stages
   constexpr int BN = 64;                  // keys per sequence block
   constexpr int NKC = D / 16;             // 16-wide k-chunks over d
   constexpr int NDT = D / 32;             // 32-row tiles of O^T over d
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TILE = BN * D;            // elements of one K (or V) block
   constexpr int SPANS = TILE / 512;        // 1 KB spans per block
-  constexpr int LOADS = (SPANS + NW - 1) / NW;
+  constexpr int LOADS = (SPANS + NR - 1) / NR;   // the waves of a stage set load its blocks
 
   // Each K stage as two 32-row halves and each V stage as one array, all
   // separate objects: in every block the loads in flight go to (K stage ST,
   // half 0), (K stage ST^1, half 1) and V stage ST^1 while the reads come from
   // the other three, so the compiler can see that no read waits for them.
-  __shared__ __attribute__((aligned(1024))) bf16 smemK00[TILE / 2];
-  __shared__ __attribute__((aligned(1024))) bf16 smemK01[TILE / 2];
-  __shared__ __attribute__((aligned(1024))) bf16 smemK10[TILE / 2];
-  __shared__ __attribute__((aligned(1024))) bf16 smemK11[TILE / 2];
-  __shared__ __attribute__((aligned(1024))) bf16 smemV0[TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 smemV1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK00[NS * TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK01[NS * TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK10[NS * TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemK11[NS * TILE / 2];
+  __shared__ __attribute__((aligned(1024))) bf16 smemV0[NS * TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 smemV1[NS * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 31;
   const int hh = lane >> 5;
+  const int rw = KS ? (wave & 3) : wave;  // row group of the tile
+  const int kh = KS ? (wave >> 2) : 0;    // key half (stage set) of the wave
 
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH;
@@ -147,8 +156,8 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int T = p.T;
   const long long TG = (long long)T * G;
 
-  const long long R0 = (long long)tile * (NW * 32);
-  const long long Rw = R0 + wave * 32;
+  const long long R0 = (long long)tile * (NR * 32);
+  const long long Rw = R0 + rw * 32;
   const long long R = Rw + n;
   const bool row_ok = R < TG;
   const bool wave_active = Rw < TG;
@@ -156,7 +165,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int hq = kvh * G + (row_ok ? (int)(R % G) : 0);
   const int tw_min = wave_active ? (int)(Rw / G) : T - 1;
   const int tw_max = wave_active ? (int)((Rw + 31 < TG ? Rw + 31 : TG - 1) / G) : T - 1;
-  const long long Rlast = (R0 + NW * 32 < TG ? R0 + NW * 32 : TG) - 1;
+  const long long Rlast = (R0 + NR * 32 < TG ? R0 + NR * 32 : TG) - 1;
   const int t_first = (int)(R0 / G);
   const int t_last = (int)(Rlast / G);
   const int nblocks = t_last / BN + 1;
@@ -164,6 +173,11 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int jm = (t_first + 1) / BN < nblocks ? (t_first + 1) / BN : nblocks;
   // key blocks [jlo, jhi) swept by this workgroup
   int jlo = 0, jhi = nblocks;
+  if constexpr (KS) {
+    // set 0 the first half of the key blocks, set 1 the rest (and the masked ones)
+    if (kh == 0) jhi = nblocks / 2;
+    else jlo = nblocks / 2;
+  }
   if constexpr (SPLIT) {
     if (part >= 0) {
       const int j_tile = p.ntiles - 1 - tile;          // the short partner tile
@@ -202,7 +216,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   uint32_t offk[LOADS], offv[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int sp = i * NW + wave;
+    const int sp = i * NR + rw;
     const int r = sp * 4 + lane / 16;
     const int pc = lane % 16;
     offk[i] = (uint32_t)(r * (int)kstride + (pc ^ (r & 15)) * 8) * 2u;
@@ -224,19 +238,19 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   // compile time (no branch per load: fewer basic blocks in the sweep for
   // the scheduler to work across)
   auto dma_rows = [&]<int S_LO, int S_HI>(const bf16* head, int blk, const uint32_t (&off)[LOADS], bf16* lbase) {
-    static_assert(S_LO % NW == 0 && S_HI % NW == 0, "span ranges are whole rounds of the waves");
+    static_assert(S_LO % NR == 0 && S_HI % NR == 0, "span ranges are whole rounds of the waves");
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(head, blk);
 #pragma unroll
-    for (int i = S_LO / NW; i < S_HI / NW; ++i) dma16(rs, off[i], lbase + (i * NW + wave - S_LO) * 512);
+    for (int i = S_LO / NR; i < S_HI / NR; ++i) dma16(rs, off[i], lbase + (i * NR + rw - S_LO) * 512);
   };
 
   const int klast = jhi - 1;
   auto clampb = [&](int blk) { return blk <= klast ? blk : klast; };
   // K stage st, half h (rows 32h .. 32h+31 of the block)
   auto khalf = [&](int st, int h) -> bf16* {
-    return st ? (h ? smemK11 : smemK10) : (h ? smemK01 : smemK00);
+    return (st ? (h ? smemK11 : smemK10) : (h ? smemK01 : smemK00)) + (KS ? kh * (TILE / 2) : 0);
   };
-  auto vst = [&](int st) { return st ? smemV1 : smemV0; };
+  auto vst = [&](int st) { return (st ? smemV1 : smemV0) + (KS ? kh * TILE : 0); };
 
   // Lane-constant LDS byte offsets.
   //  K operand row r = pi(n) of a 32-row half: chunk (2kc + hh) ^ (r & 15);
@@ -321,7 +335,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   // V^T operand fragments of one 32-key half-block H of V stage ST, read ahead
   // of the softmax whose probabilities they multiply
   auto vload = [&]<int ST, int H>(bf16x8 (&vf)[2 * NDT]) {
-    const char* vb = reinterpret_cast<const char*>(ST ? smemV1 : smemV0) + H * 32 * D * 2;
+    const char* vb = reinterpret_cast<const char*>((ST ? smemV1 : smemV0) + (KS ? kh * TILE : 0)) + H * 32 * D * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -342,9 +356,21 @@ void moda_fwd_bf16_kernel(FwdParams p) {
 
   // ---- prologue: K(jlo) both halves, K(jlo+1) first half, V(jlo) ----
   // (stage of block j: (j - jlo) & 1)
-  const bool sweep = jlo < jhi;                     // workgroup-uniform
+  const bool sweep = jlo < jhi;                     // uniform over the stage set
   float s_a[16], s_b[16];
-  if (sweep) {
+  if constexpr (KS) {
+    // both stage sets take every barrier, a set without blocks too
+    if (sweep) {
+      dma_rows.template operator()<0, 8>(kbase, jlo, offk, khalf(0, 0));
+      dma_rows.template operator()<8, 16>(kbase, jlo, offk, khalf(0, 1));
+      dma_rows.template operator()<0, 8>(kbase, clampb(jlo + 1), offk, khalf(1, 0));
+      dma_rows.template operator()<0, 16>(vbase, jlo, offv, vst(0));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (sweep) qk.template operator()<0, 0>(s_a);
+    __syncthreads();
+  } else if (sweep) {
     dma_rows.template operator()<0, 8>(kbase, jlo, offk, khalf(0, 0));
     dma_rows.template operator()<8, 16>(kbase, jlo, offk, khalf(0, 1));
     dma_rows.template operator()<0, 8>(kbase, clampb(jlo + 1), offk, khalf(1, 0));
@@ -394,6 +420,10 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     block.template operator()<true, 1>(j + 1);
   }
   if (j < jhi) { block.template operator()<true, 0>(j); ++j; }
+  if constexpr (KS) {
+    // set 1 sweeps at most one block more than set 0: set 0 takes its barrier
+    if (kh == 0 && nblocks - 2 * (nblocks / 2) > 0) __syncthreads();
+  }
 
   // ---- depth fold: this wave's positions only (see moda_fwd.hpp) ----
   if (wave_active && p.L_d > 0 && part != 0) {
@@ -409,6 +439,9 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     static_assert(NW <= 8, "one 8 KB region per wave in the 64 KB of stages");
     for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
       if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
+      if constexpr (KS) {
+        if ((int)(((n0 - (nlo & ~31LL)) >> 5) & 1) != kh) continue;   // the sets take alternate tiles
+      }
       // K operand fragments (rows n0 + key_row) and this lane's share of the
       // 32 value rows (row n0 + 4 i + lane / 16, chunk lane % 16), loaded
       // together: one round trip to memory per tile
@@ -501,6 +534,36 @@ void moda_fwd_bf16_kernel(FwdParams p) {
         for (int dt = 0; dt < NDT; ++dt)
           o[dt] = mma16(tr_frag(reinterpret_cast<const char*>(vwave) + c * 16 * D * 2 + va[dt]), pf[c], o[dt]);
     }
+  }
+
+  if constexpr (KS) {
+    // set 1 hands its state (O, m, l per lane) to set 0 through LDS, which
+    // merges it as the online-softmax recurrence over the union of the two
+    // key sets (set 0's values first, so the result does not depend on
+    // timing) and writes the output.  The stages are free once every fold
+    // is done.
+    __syncthreads();
+    float* so = reinterpret_cast<float*>((rw & 1 ? smemV1 : smemV0) + (rw < 2 ? TILE : 0));
+    float* sm = reinterpret_cast<float*>(smemK00) + rw * 128;
+    if (kh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) so[(dt * 16 + i) * 64 + lane] = o[dt][i];
+      sm[lane] = m_run;
+      sm[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m_o = sm[lane], l_o = sm[64 + lane];
+    const float m_new = fmaxf(m_run, m_o);
+    const float a = __builtin_amdgcn_exp2f(m_run - m_new), c = __builtin_amdgcn_exp2f(m_o - m_new);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = __builtin_fmaf(a, o[dt][i], c * so[(dt * 16 + i) * 64 + lane]);
+    l_run = __builtin_fmaf(a, l_run, c * l_o);
+    m_run = m_new;
   }
 
   if constexpr (SPLIT) {

@@ -123,9 +123,12 @@ int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
 
 /*
  * moda_fwd_workspace_bytes -- size in bytes of the workspace that moda_fwd_ws
- * uses for these sizes, or -1 for invalid sizes.  0 when every query tile runs
- * whole anyway: grids of more than two workgroups per compute unit (about
- * T * Hq / Hkv * B * Hkv > 65536 rows), shapes other than bf16 with d = 128.
+ * uses for these sizes, or -1 for invalid sizes.  0 when no query tile is
+ * split across workgroups: grids of more than two workgroups per compute
+ * unit (about T * Hq / Hkv * B * Hkv > 65536 rows), grids small enough for
+ * one round of eight-wave workgroups over 128-row tiles (at most 256 such
+ * tiles: there moda_fwd itself splits each tile's keys between the two
+ * halves of its workgroup), shapes other than bf16 with d = 128.
  * The size depends on B, T, G = Hq / Hkv and Hkv only: a 4096-byte header
  * of arrival counters (the same for every shape), then 2 * 66 * 64 * 4 =
  * 33792 bytes per (split tile, wave) for the two parts' states.  Splitting

@@ -224,7 +224,8 @@ def test_fwd_workspace_validation():
     # 4096-byte counter header + two 66 x 64 float states per (split tile, wave)
     units = 2 * 128 * 4                       # B = 1, T = 4096, G = 8, Hkv = 2: 128 split tiles per kv head
     assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, 1) == 4096 + units * 33792
-    assert lib.moda_fwd_workspace_bytes(1, 1000, 8, 1, 128, 1) == 4096 + 31 * 4 * 33792
+    assert lib.moda_fwd_workspace_bytes(5, 1000, 8, 1, 128, 1) == 4096 + 5 * 31 * 4 * 33792
+    assert lib.moda_fwd_workspace_bytes(1, 1000, 8, 1, 128, 1) == 0       # one round: split inside the workgroup
     assert lib.moda_fwd_workspace_bytes(1, 65536, 16, 2, 128, 1) == 0     # big grid: whole tiles
     assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, 0) == 0      # float32: generic kernel
     assert lib.moda_fwd_workspace_bytes(1, 4096, 16, 2, 64, 1) == 0       # d = 64: generic kernel

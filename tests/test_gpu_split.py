@@ -55,14 +55,15 @@ def test_split_workload_T4096_all_rows():
 
 
 EDGE = [
-    # B, T, Hq, Hkv, L_d (bf16, d = 128)
-    (1, 1000, 8, 1, 5),      # G = 8, ragged last tile
-    (2, 777, 2, 2, 0),       # G = 1, no depth
-    (1, 300, 32, 1, 3),      # G = 32
-    (1, 130, 64, 1, 2),      # G = 64: two positions per 128-row tile
-    (3, 257, 16, 2, 24),     # B = 3, odd tile count per (b, kv head)
-    (1, 129, 4, 4, 33),      # G = 1, L_d > 32
-    (1, 40, 12, 1, 3),       # G = 12, few tiles: the split parts of short tiles
+    # B, T, Hq, Hkv, L_d (bf16, d = 128); B large enough for two rounds of
+    # 128-row tiles (a grid of one round splits inside the workgroup instead)
+    (5, 1000, 8, 1, 5),      # G = 8, ragged last tile
+    (19, 777, 2, 2, 0),      # G = 1, no depth
+    (4, 300, 32, 1, 3),      # G = 32
+    (4, 130, 64, 1, 2),      # G = 64: two positions per 128-row tile
+    (8, 257, 16, 2, 24),     # odd tile count per (b, kv head)
+    (33, 129, 4, 4, 33),     # G = 1, L_d > 32
+    (65, 40, 12, 1, 3),      # G = 12, few tiles: the split parts of short tiles
     (1, 1, 8, 2, 3),         # one position: one tile, nothing to split
     (2, 2048, 16, 4, 7),     # G = 4, 8 (b, kv head) x 64 tiles: the largest split grid (512)
 ]
@@ -72,6 +73,7 @@ EDGE = [
 def test_split_edge_shapes(case):
     B, T, Hq, Hkv, L_d = case
     need = moda.fwd_workspace_bytes(B, T, Hq, Hkv, 128, torch.bfloat16)
+    assert need > 0 or T == 1
     _say(f"split edge {case} (workspace {need} bytes)")
     inputs = make_inputs(B, T, Hq, Hkv, 128, L_d, dtype="bf16", seed=90 + T + L_d)
     out, lse = _run_ws(inputs)
@@ -116,3 +118,18 @@ def test_split_repeated_calls_agree():
     assert float((o0.float() - o1.float()).abs().max()) <= tol
     assert float((l0 - l1).abs().max()) <= tol
     assert np32(o1).shape == (1, 4096, 16, 128)
+
+
+def test_one_round_grid_needs_no_workspace():
+    """A grid that fits one round of eight-wave workgroups splits each tile's
+    keys inside the workgroup: no workspace, and moda_fwd_ws gives moda_fwd's
+    results bit for bit."""
+    B, T, Hq, Hkv, L_d = 1, 1000, 8, 1, 5
+    assert moda.fwd_workspace_bytes(B, T, Hq, Hkv, 128, torch.bfloat16) == 0
+    _say("one-round grid: moda_fwd_ws == moda_fwd")
+    q, ks, vs, kd, vd = [x.cuda() for x in make_inputs(B, T, Hq, Hkv, 128, L_d, dtype="bf16", seed=77)]
+    packed = moda.moda_pack_depth(kd, vd)
+    o1, l1 = moda.moda_fwd(q, ks, vs, *packed, L_d)
+    o2, l2 = moda.moda_fwd(q, ks, vs, *packed, L_d, work=moda.fwd_workspace(q, ks))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
