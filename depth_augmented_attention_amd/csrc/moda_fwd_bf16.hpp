@@ -55,6 +55,13 @@
 //     l likewise: the same online-softmax recurrence over the union of the
 //     two key sets, exact in real arithmetic -- writes out and lse, and
 //     clears the counter for the next launch.
+//   * Key split inside the workgroup (KS, grids of at most one round of
+//     eight-wave workgroups over 128-row tiles): the two sets of four waves
+//     share a tile's rows, sweep one half of its key blocks each (with their
+//     own LDS stages) and take alternate depth tiles; set 1 hands its state
+//     to set 0 through LDS, which merges it with the same recurrence and
+//     writes the output.  No workspace, and one barrier count for both sets
+//     (the set with one block fewer takes one barrier more).
 #pragma once
 
 #include "moda_common.hpp"
