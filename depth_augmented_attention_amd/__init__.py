@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     status_string,
 )
 from .ops import (  # noqa: F401
+    bwd_workspace,
+    bwd_workspace_bytes,
     depth_packed_elems,
     fwd_workspace,
     fwd_workspace_bytes,

@@ -21,7 +21,7 @@ MODA_ERR_WORKSPACE = 6
 # every symbol include/moda.h declares
 EXPORTS = ("moda_depth_packed_elems", "moda_pack_depth", "moda_fwd", "moda_fwd_workspace_bytes", "moda_fwd_ws",
            "moda_fwd_window",
-           "moda_append_depth", "moda_bwd", "moda_bwd_noalloc", "moda_bwd_window", "moda_pack_depth_q8", "moda_fwd_q8",
+           "moda_append_depth", "moda_bwd", "moda_bwd_workspace_bytes", "moda_bwd_ws", "moda_bwd_noalloc", "moda_bwd_window", "moda_pack_depth_q8", "moda_fwd_q8",
            "moda_fwd_window_q8", "moda_append_depth_q8", "moda_bwd_q8", "moda_bwd_window_q8",
            "moda_status_string")
 
@@ -62,6 +62,10 @@ def load() -> ctypes.CDLL:
     lib.moda_append_depth.restype = c_int
     lib.moda_bwd.argtypes = [c_vp] * 14 + [c_int] * 7 + [c_vp]
     lib.moda_bwd.restype = c_int
+    lib.moda_bwd_workspace_bytes.argtypes = [c_int] * 6
+    lib.moda_bwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.moda_bwd_ws.argtypes = [c_vp] * 13 + [c_int] * 7 + [c_vp, ctypes.c_longlong, c_vp]
+    lib.moda_bwd_ws.restype = c_int
     lib.moda_bwd_noalloc.argtypes = [c_vp] * 13 + [c_int] * 7 + [c_vp]
     lib.moda_bwd_noalloc.restype = c_int
     lib.moda_pack_depth_q8.argtypes = [c_vp] * 6 + [c_int] * 6 + [c_vp]

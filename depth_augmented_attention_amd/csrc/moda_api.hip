@@ -95,6 +95,45 @@ SplitPlan split_plan(int dtype, int d, long long rows, long long BH) {
   return sp;
 }
 
+// Which dK/dV kernel the backward runs for bf16 with d = 128: the kernel laid
+// out for the gfx950 memory path addresses one kv head's lse rows with 32-bit
+// offsets, and with G not dividing 64 also one batch's q / dO rows (with G
+// dividing 64 those offsets stay within one 64-row block).
+enum class DkdvForm { generic, whole_positions, any_g };
+DkdvForm dkdv_form(int dtype, int d, int T, int G, int Hq) {
+  if (dtype != MODA_BF16 || d != 128) return DkdvForm::generic;
+  const bool lse32 = (long long)T * G * 4 < 0x7fffffffLL;
+  const bool q32 = (long long)T * Hq * d * 2 < 0x7fffffffLL;
+  if (lse32 && 64 % G == 0) return DkdvForm::whole_positions;
+  if (lse32 && q32) return DkdvForm::any_g;
+  return DkdvForm::generic;
+}
+
+// The backward's workspace (moda_bwd_ws): the work buffer (2 * B * Hq * T
+// floats, padded to 256 bytes), then, when the dK/dV rows are split, 128 KiB
+// of float32 partial sums per (chunk, b, kv head).  One dK/dV workgroup runs
+// per compute unit.
+struct BwdWsPlan {
+  moda::BwdSplitPlan split;
+  long long work_bytes = 0;
+  long long bytes = 0;
+};
+BwdWsPlan bwd_ws_plan(int B, int T, int Hq, int Hkv, int d, int dtype) {
+  BwdWsPlan wp;
+  const int G = Hq / Hkv;
+  const long long work = smul(2LL * B, Hq, T, 4);
+  if (work > LLONG_MAX / 2) {                   // saturated: no such buffer
+    wp.work_bytes = wp.bytes = LLONG_MAX;
+    return wp;
+  }
+  wp.work_bytes = (work + 255) / 256 * 256;
+  if (dkdv_form(dtype, d, T, G, Hq) != DkdvForm::generic)
+    wp.split = moda::bwd_split_plan(T, G, (long long)B * Hkv, (int)cdiv(T, 128), (int)kCUs);
+  const long long part = smul((long long)B * Hkv, wp.split.items, 32768 * 4);
+  wp.bytes = part > LLONG_MAX - wp.work_bytes ? LLONG_MAX : wp.work_bytes + part;
+  return wp;
+}
+
 template <typename E, int D>
 hipError_t launch_fwd(const moda::FwdParams& p, unsigned grid, int nw, hipStream_t s) {
   if constexpr (sizeof(E) == 2 && D == 128) {
@@ -140,18 +179,24 @@ hipError_t launch_bwd(const moda::BwdParams& p, hipStream_t s) {
   else
     hipLaunchKernelGGL((moda::moda_bwd_dq_kernel<E, D, kWaves>), dim3(BH * p.ntiles), dim3(kWaves * 64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // the bf16 d=128 kernel addresses one kv head's lse rows with 32-bit
-  // offsets; with G not dividing 64 also one batch's q / dO rows (with G
-  // dividing 64 those offsets stay within one 64-row block)
-  const bool lse32 = (long long)p.T * p.G * 4 < 0x7fffffffLL;
-  const bool q32 = (long long)p.T * p.Hq * D * 2 < 0x7fffffffLL;
   if constexpr (sizeof(E) == 2 && D == 128) {
-    if (lse32 && 64 % p.G == 0)
+    const DkdvForm form = dkdv_form(MODA_BF16, D, p.T, p.G, p.Hq);
+    if (p.kchunk > 0) {
+      // row-split: chunk_items workgroups per (b, kv head), then the sums
+      const unsigned grid = BH * (unsigned)p.kitems;
+      if (form == DkdvForm::whole_positions)
+        hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, true, true>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+      else
+        hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, false, true>), dim3(grid), dim3(kWaves * 64), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((moda::moda_bwd_dkdv_reduce_kernel<D>), dim3(BH * p.nktiles), dim3(256), 0, s, p);
+    } else if (form == DkdvForm::whole_positions) {
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, true>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
-    else if (lse32 && q32)
+    } else if (form == DkdvForm::any_g) {
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_bf16_kernel<D, false>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
-    else
+    } else {
       hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
+    }
   } else {
     hipLaunchKernelGGL((moda::moda_bwd_dkdv_kernel<E, D, kWaves>), dim3(BH * p.nktiles), dim3(kWaves * 64), 0, s, p);
   }
@@ -425,20 +470,24 @@ static int device_scratch(float** ptr) {
 }
 
 // work == nullptr with use_scratch: the work buffer is the device's static
-// scratch (checked against its size after the other arguments).
+// scratch (checked against its size after the other arguments).  With use_ws
+// the work buffer and the row-split dK/dV partial sums come from the caller's
+// workspace ws of ws_bytes bytes (bwd_ws_plan).
 static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                     const void* v_depth, const float* k_scale, const float* v_scale, int q8,
                     const void* out, const float* lse, const void* dout, void* dq,
                     void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, float* work, int B,
                     int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi, int dtype,
-                    void* stream, bool use_scratch = false) {
+                    void* stream, bool use_scratch = false, void* ws = nullptr, long long ws_bytes = 0,
+                    bool use_ws = false) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || L_cap < 0) return MODA_ERR_SHAPE;
   if (slot_lo < 0 || slot_hi < slot_lo || slot_hi > L_cap) return MODA_ERR_SHAPE;
   if ((long long)T * L_cap > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;   // packed key index is 31-bit
   if (Hq % Hkv != 0) return MODA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return MODA_ERR_DTYPE;
   if (!supported_d(d)) return MODA_ERR_UNSUPPORTED;
-  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq || (!work && !use_scratch))
+  if (!q || !k_seq || !v_seq || !out || !lse || !dout || !dq || !dk_seq || !dv_seq ||
+      (!work && !use_scratch && !use_ws))
     return MODA_ERR_NULL;
   const int L_d = slot_hi - slot_lo;
   if (L_d > 0 && (!k_depth || !v_depth || !dk_depth || !dv_depth)) return MODA_ERR_NULL;
@@ -457,6 +506,16 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
     const int st = device_scratch(&work);
     if (st != MODA_OK) return st;
   }
+  moda::BwdSplitPlan split;
+  float* part = nullptr;
+  if (use_ws) {
+    const BwdWsPlan wp = bwd_ws_plan(B, T, Hq, Hkv, d, dtype);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < wp.bytes) return MODA_ERR_WORKSPACE;
+    if (smul(BH, wp.split.items) > 0x7fffffffLL) return MODA_ERR_SHAPE;
+    work = static_cast<float*>(ws);
+    split = wp.split;
+    if (split.C > 0) part = reinterpret_cast<float*>(static_cast<char*>(ws) + wp.work_bytes);
+  }
 
   moda::BwdParams p;
   p.q = q; p.k = k_seq; p.v = v_seq; p.kd = k_depth; p.vd = v_depth;
@@ -471,6 +530,10 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   div_magic(G, &p.g_magic, &p.g_shift);
+  p.part = part;
+  p.kchunk = split.C;
+  p.kfull = split.full;
+  p.kitems = split.items;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -488,6 +551,23 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq, const void* k_
   if (L_d < 0) return MODA_ERR_SHAPE;
   return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
                   dv_seq, dk_depth, dv_depth, work, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream);
+}
+
+long long moda_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int dtype) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv != 0) return -1;
+  if (!valid_dtype(dtype)) return -1;
+  const long long n = bwd_ws_plan(B, T, Hq, Hkv, d, dtype).bytes;
+  return n == LLONG_MAX ? -1 : n;
+}
+
+int moda_bwd_ws(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
+                const void* v_depth, const void* out, const float* lse, const void* dout, void* dq,
+                void* dk_seq, void* dv_seq, void* dk_depth, void* dv_depth, int B, int T, int Hq,
+                int Hkv, int d, int L_d, int dtype, void* work, long long work_bytes, void* stream) {
+  if (L_d < 0) return MODA_ERR_SHAPE;
+  return bwd_impl(q, k_seq, v_seq, k_depth, v_depth, nullptr, nullptr, 0, out, lse, dout, dq, dk_seq,
+                  dv_seq, dk_depth, dv_depth, nullptr, B, T, Hq, Hkv, d, L_d, 0, L_d, dtype, stream, false,
+                  work, work_bytes, true);
 }
 
 int moda_bwd_noalloc(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,

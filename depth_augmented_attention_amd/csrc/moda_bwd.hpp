@@ -36,6 +36,7 @@
 
 #include <utility>
 
+#include "moda_bwd_split.hpp"
 #include "moda_common.hpp"
 #include "moda_fwd.hpp"        // depth_tile_used
 #include "moda_fwd_bf16.hpp"   // direct-to-LDS loads, LDS transpose reads
@@ -70,6 +71,12 @@ struct BwdParams {
   float scale_log2;    // log2(e) / sqrt(d)
   uint32_t g_magic;    // x / G == (x * g_magic) >> g_shift for 0 <= x < 2^31
   int g_shift;
+  // row-split dK/dV (short sequences): each key tile's query blocks are cut
+  // into chunks of kchunk blocks swept by separate workgroups
+  float* part;         // fp32 partial dK / dV, 32768 floats per (chunk, b, kv head)
+  int kchunk;          // query blocks per chunk, a multiple of 2G; 0: no split
+  int kfull;           // full chunks over all key tiles of one (b, kv head)
+  int kitems;          // chunks (full and remainder) of one (b, kv head)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -731,7 +738,7 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, v
 
 }  // namespace bwdbf16
 
-template <int D, bool GP>
+template <int D, bool GP, bool SPLIT = false>
 __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   static_assert(D == 128, "built for head size 128");
   using namespace bwdbf16;
@@ -761,7 +768,24 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
 
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH;
-  const int ktile = (int)(blockIdx.x / BH);     // earliest keys (most rows) first
+  // SPLIT: blocks [q_lo, q_hi) of the tile's sweep (chunks of the row-split
+  // map); otherwise every block, the earliest keys (most rows) first
+  int ktile = (int)(blockIdx.x / BH), q_lo = 0, q_hi = 0, nchunks = 1;
+  if constexpr (SPLIT) {
+    const BwdChunkMap cm(p.T, p.G, p.kchunk, p.nktiles);
+    const int item = ktile;
+    if (item < p.kfull) {
+      ktile = cm.full_tile(item);
+      q_lo = (item - cm.prefix(ktile)) * p.kchunk;
+      q_hi = q_lo + p.kchunk;
+    } else {
+      ktile = cm.rem_tile(item - p.kfull);
+      if (ktile < 0) return;                    // past the map (not launched)
+      q_lo = cm.nf(ktile) * p.kchunk;
+      q_hi = cm.nqb(ktile);
+    }
+    nchunks = cm.nchunks(ktile);
+  }
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;
@@ -878,6 +902,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   const float sl2 = p.scale_log2;
   const int rb0 = kt0 * G / QB * QB;            // first block with a row at position >= kt0
   const int nqb = (TG - rb0 + QB - 1) / QB;
+  if constexpr (!SPLIT) q_hi = nqb;
 
   // S and dP of 32-row sub-block `sub` of the block in stage ST, their
   // accumulators seeded with -lse*sqrt(d) and -Delta of each row: s holds
@@ -983,7 +1008,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
     // that the workgroups of all key tiles read the same rows at about the
     // same time (they share them in L2) and the masked blocks come last
     const int Rb = rb0 + (nqb - 1 - qb) * QB;
-    if (qb + 1 < nqb) load_block(Rb - QB, ST ^ 1);
+    if (qb + 1 < q_hi) load_block(Rb - QB, ST ^ 1);
     if (Rb + QB - 1 >= wkey0 * G) {             // some row of the block sees some key of this wave
       if (Rb >= (wkey0 + 31) * G)               // every row sees every key of this wave
         compute.template operator()<ST, false>(Rb);
@@ -994,17 +1019,30 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
     __syncthreads();
   };
 
-  load_block(rb0 + (nqb - 1) * QB, 0);
+  load_block(rb0 + (nqb - 1 - q_lo) * QB, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int qb = 0;
-  for (; qb + 1 < nqb; qb += 2) {
+  int qb = q_lo;
+  for (; qb + 1 < q_hi; qb += 2) {
     block.template operator()<0>(qb);
     block.template operator()<1>(qb + 1);
   }
-  if (qb < nqb) block.template operator()<0>(qb);
+  if (qb < q_hi) block.template operator()<0>(qb);
 
-  if (key_ok) {
+  if (SPLIT && nchunks > 1) {
+    // partial sums in the accumulators' own layout, [wave][dK, dV][dt][4][lane][4]
+    // floats (whole 1 KB rows per store), added up by moda_bwd_dkdv_reduce_kernel
+    float* pp = p.part + (size_t)blockIdx.x * 32768 + wave * 8192 + lane * 4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 k4 = {dk[dt][g4 * 4 + 0], dk[dt][g4 * 4 + 1], dk[dt][g4 * 4 + 2], dk[dt][g4 * 4 + 3]};
+        const f32x4 v4 = {dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(pp + (dt * 4 + g4) * 256) = k4;
+        *reinterpret_cast<f32x4*>(pp + (16 + dt * 4 + g4) * 256) = v4;
+      }
+  } else if (key_ok) {
     const float sc = p.scale;
     const long long orow = (((long long)b * T + key) * p.Hkv + kvh) * D;
     bf16* dkp = reinterpret_cast<bf16*>(p.dk) + orow;
@@ -1019,6 +1057,55 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
         store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
       }
   }
+}
+
+// Row-split dK/dV: the sum of a key tile's partial sums, in chunk order (its
+// full chunks, then its remainder chunk), scaled and stored like the unsplit
+// kernel's epilogue.  One workgroup per (key tile, b, kv head); tiles swept by
+// a single chunk were stored by the dK/dV kernel itself.
+template <int D>
+__global__ __launch_bounds__(256) void moda_bwd_dkdv_reduce_kernel(BwdParams p) {
+  static_assert(D == 128, "built for head size 128");
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int kt = (int)(blockIdx.x / BH);
+  const BwdChunkMap cm(p.T, p.G, p.kchunk, p.nktiles);
+  const int nf = cm.nf(kt);
+  const bool has_rem = cm.rem(kt) > 0;
+  if (nf + (has_rem ? 1 : 0) <= 1) return;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const size_t first = (size_t)cm.prefix(kt) * BH + bh;             // slot of full chunk 0
+  const size_t last = ((size_t)p.kfull + cm.rem_rank(kt)) * BH + bh;  // slot of the remainder
+  const float* base = p.part + wave * 8192 + lane * 4;
+  f32x4 acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto add = [&](size_t slot) {
+    const float* src = base + slot * 32768;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] += *reinterpret_cast<const f32x4*>(src + i * 256);
+  };
+  for (int c = 0; c < nf; ++c) add(first + (size_t)c * BH);
+  if (has_rem) add(last);
+
+  const int key = kt * 128 + wave * 32 + (lane & 31);
+  if (key >= p.T) return;
+  const int hh = lane >> 5;
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const float sc = p.scale;
+  const long long orow = (((long long)b * p.T + key) * p.Hkv + kvh) * D;
+  bf16* dkp = reinterpret_cast<bf16*>(p.dk) + orow;
+  bf16* dvp = reinterpret_cast<bf16*>(p.dv) + orow;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int e = dt * 32 + g4 * 8 + hh * 4;
+      const f32x4 k4 = acc[dt * 4 + g4], v4 = acc[16 + dt * 4 + g4];
+      store4(dkp + e, k4[0] * sc, k4[1] * sc, k4[2] * sc, k4[3] * sc);
+      store4(dvp + e, v4[0], v4[1], v4[2], v4[3]);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -210,7 +210,8 @@ def _fwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, ou
 def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
              k_depth: torch.Tensor | None, v_depth: torch.Tensor | None, L_d: int,
              out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
-             grads: tuple | None = None, work: torch.Tensor | None = None, stream=None):
+             grads: tuple | None = None, work: torch.Tensor | None = None, stream=None,
+             workspace: torch.Tensor | None = None):
     """Gradients of the MoDA forward.
 
     q, k_seq, v_seq and the packed depth buffers as for moda_fwd; out and lse
@@ -220,9 +221,33 @@ def moda_bwd(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
     in the logical depth layout (one slot per earlier layer), or None when
     L_d == 0.  `grads` may supply those five output tensors; `work` a float32
     [2,B,Hq,T] scratch tensor.
+
+    workspace: optional workspace from bwd_workspace(q, k_seq) (instead of
+    `work`) -- the call then goes to moda_bwd_ws, which splits each key
+    tile's query rows over several workgroups on short sequences.
     """
+    if workspace is not None:
+        if work is not None:
+            raise ValueError("pass either work or workspace")
+        return _bwd_call("moda_bwd_ws", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, dout, grads,
+                         False, stream, workspace=workspace)
     return _bwd_call("moda_bwd", q, k_seq, v_seq, k_depth, v_depth, L_d, 0, L_d, out, lse, dout, grads, work,
                      stream)
+
+
+def bwd_workspace_bytes(B: int, T: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype) -> int:
+    n = load().moda_bwd_workspace_bytes(B, T, Hq, Hkv, d, _DT.get(dtype, -1))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def bwd_workspace(q: torch.Tensor, k_seq: torch.Tensor) -> torch.Tensor:
+    """A workspace for moda_bwd(..., workspace=...) on these shapes (uint8 on
+    q's device, uninitialised: every byte the call reads it writes first)."""
+    B, T, Hq, d = q.shape
+    return torch.empty(bwd_workspace_bytes(B, T, Hq, k_seq.shape[2], d, q.dtype), dtype=torch.uint8,
+                       device=q.device)
 
 
 def moda_bwd_noalloc(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
@@ -312,9 +337,9 @@ def moda_bwd_window(q: torch.Tensor, k_seq: torch.Tensor, v_seq: torch.Tensor,
 
 
 def _bwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, out, lse, dout, grads, work,
-              stream):
-    """Checks and the call of moda_bwd (fn = "moda_bwd": L_cap slots, all
-    read) or moda_bwd_window."""
+              stream, workspace=None):
+    """Checks and the call of moda_bwd / moda_bwd_ws (L_cap slots, all read;
+    work False and a workspace for moda_bwd_ws) or moda_bwd_window."""
     (B, T, Hq, Hkv, d, L_d), grads, work = _bwd_common(q, k_seq, v_seq, slot_lo, slot_hi, out, lse, dout,
                                                        grads, work)
     kd_ptr = vd_ptr = None
@@ -328,6 +353,17 @@ def _bwd_call(fn, q, k_seq, v_seq, k_depth, v_depth, L_cap, slot_lo, slot_hi, ou
                 raise ValueError(f"{name} must be a packed buffer of {n} elements of {q.dtype}")
         kd_ptr, vd_ptr = k_depth.data_ptr(), v_depth.data_ptr()
     ptr = [g.data_ptr() if g is not None else None for g in grads]
+    if fn == "moda_bwd_ws":
+        _dev(workspace, "workspace")
+        dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
+                          dout, workspace, *grads[:3], *(grads[3:] if L_d > 0 else ()))
+        st = _call(dev, fn, stream,
+            q.data_ptr(), k_seq.data_ptr(), v_seq.data_ptr(), kd_ptr, vd_ptr,
+            out.data_ptr(), lse.data_ptr(), dout.data_ptr(), ptr[0], ptr[1], ptr[2],
+            ptr[3], ptr[4], B, T, Hq, Hkv, d, L_cap, _dtype_code(q),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        check(st, fn)
+        return grads
     dev = _one_device(q, k_seq, v_seq, k_depth if kd_ptr else None, v_depth if vd_ptr else None, out, lse,
                       dout, work, *grads[:3], *(grads[3:] if L_d > 0 else ()))
     slots = (L_cap,) if fn == "moda_bwd" else (L_cap, slot_lo, slot_hi)

@@ -299,6 +299,53 @@ int moda_bwd(const void* q, const void* k_seq, const void* v_seq,
              void* stream);
 
 /*
+ * moda_bwd_workspace_bytes -- size in bytes of the workspace that moda_bwd_ws
+ * uses for these sizes, or -1 for invalid sizes.  Always at least the work
+ * buffer, 2 * B * Hq * T float32 rounded up to 256 bytes; on short sequences
+ * with bf16 and d = 128 (about B * Hkv * T / 128 < 410 key tiles) another
+ * 131072 bytes per chunk of the row-split dK / dV (described at moda_bwd_ws),
+ * of which there are at most 256 + B * Hkv * ceil(T / 128).
+ */
+long long moda_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int dtype);
+
+/*
+ * moda_bwd_ws -- moda_bwd with a workspace, for short sequences.
+ *
+ * moda_bwd gives each tile of 128 keys (per batch and kv head) one
+ * workgroup, which sweeps every query row that sees its keys; under the
+ * causal mask (mhpn.cn article, section 2.2) the first tile meets all T * G
+ * rows and the last only its own, and when the grid does not fill the GPU
+ * the first tiles alone set the run time (the pages name short sequences as
+ * the costly case: mhpn.cn article "动态混合深度注意力机制MoDA技术解析",
+ * section 3.1, Table 2 discussion).  Here each tile's rows are cut into
+ * chunks swept by separate workgroups, all chunks about the average work of
+ * a compute unit; dk and dv being sums over rows (the formulas at moda_bwd),
+ * each chunk's float32 partial sums go to the workspace and a second kernel
+ * adds them up in a fixed order.  Other shapes, and dtype / d other than
+ * bf16 / 128, run as moda_bwd.
+ *
+ *   q ... dv_depth, B ... dtype, stream : as for moda_bwd
+ *   work       : device scratch owned by the caller, at least
+ *                moda_bwd_workspace_bytes(B, T, Hq, Hkv, d, dtype) bytes,
+ *                256-byte aligned, any contents (every byte read is first
+ *                written by the same call).  Its first 2 * B * Hq * T floats
+ *                end as moda_bwd's work buffer does.  Calls that share a
+ *                workspace must not run at the same time.
+ *   work_bytes : size of work in bytes
+ * Errors: MODA_ERR_WORKSPACE when work is NULL, not 256-byte aligned or too
+ * small; otherwise as for moda_bwd.  Results equal moda_bwd's within
+ * floating-point rounding (the split reorders the sums of dk and dv); they
+ * are the same from call to call.
+ */
+int moda_bwd_ws(const void* q, const void* k_seq, const void* v_seq,
+                const void* k_depth, const void* v_depth,
+                const void* out, const float* lse, const void* dout,
+                void* dq, void* dk_seq, void* dv_seq,
+                void* dk_depth, void* dv_depth,
+                int B, int T, int Hq, int Hkv, int d, int L_d, int dtype,
+                void* work, long long work_bytes, void* stream);
+
+/*
  * moda_bwd_noalloc -- moda_bwd without the work argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight
  * training loops, harnesses that forbid hipMalloc).  The work buffer is

@@ -38,6 +38,11 @@ int main(void) {
   EXPECT(moda_bwd_noalloc(F, F, F, NULL, NULL, F, (const float*)F, F, F, F, F, NULL, NULL, 1, 65537, 64, 1, 128,
                           0, MODA_BF16, NULL),
          MODA_ERR_WORKSPACE);
+  EXPECT(moda_bwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_BF16) > 2LL * 16 * 4096 * 4, 1);
+  EXPECT(moda_bwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_F32), 2LL * 16 * 4096 * 4);
+  EXPECT(moda_bwd_ws(F, F, F, NULL, NULL, F, (const float*)F, F, F, F, F, NULL, NULL, 1, 4096, 16, 2, 128, 0,
+                     MODA_BF16, NULL, 1 << 30, NULL),
+         MODA_ERR_WORKSPACE);
   EXPECT(moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_BF16) > 0, 1);
   EXPECT(moda_fwd_workspace_bytes(1, 4096, 16, 2, 128, MODA_F32), 0);
   EXPECT(moda_fwd_ws(F, F, F, F, F, F, NULL, 1, 4096, 16, 2, 128, 24, MODA_BF16, NULL, 1 << 30, NULL),

@@ -39,6 +39,7 @@ int main(void) {
     const int L = sizes[i][5], dt = sizes[i][6];
     total += moda_depth_packed_elems(B, T, Hkv, d, L);
     total += moda_fwd_workspace_bytes(B, T, Hq, Hkv, d, dt);
+    total += moda_bwd_workspace_bytes(B, T, Hq, Hkv, d, dt);
     /* with L_d == 0 a repack has nothing to do and valid B, T succeed */
     if (L != 0) EXPECT_ERR(moda_pack_depth(F, F, F, F, B, T, Hkv, d, L, dt, NULL));
     EXPECT_ERR(moda_fwd(F, F, F, F, F, F, NULL, B, T, Hq, Hkv, d, L, dt, NULL));
@@ -54,6 +55,8 @@ int main(void) {
                                     NULL));
     EXPECT_ERR(moda_bwd(F, F, F, F, F, F, (const float*)F, F, F, F, F, F, F, (float*)F, B, T, Hq, Hkv, d, L, dt,
                         NULL));
+    EXPECT_ERR(moda_bwd_ws(F, F, F, F, F, F, (const float*)F, F, F, F, F, F, F, B, T, Hq, Hkv, d, L, dt, F,
+                           LLONG_MAX, NULL));
     EXPECT_ERR(moda_bwd_noalloc(F, F, F, F, F, F, (const float*)F, F, F, F, F, F, F, B, T, Hq, Hkv, d, L, dt,
                                 NULL));
     EXPECT_ERR(moda_bwd_window_q8(F, F, F, (int8_t*)F, (int8_t*)F, (float*)F, (float*)F, F, (const float*)F, F,

@@ -254,3 +254,28 @@ def test_bwd_noalloc_validation():
     assert lib.moda_bwd_noalloc(*([FAKE] * 10), None, None, None, 1, 64, 4, 1, 128, 0, 1, None) \
         == _lib.MODA_ERR_NULL
     assert lib.moda_bwd_noalloc(*args, 1, 64, 4, 1, 96, 0, 1, None) == _lib.MODA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_validation():
+    lib = _lib.load()
+    work = lambda B, T, Hq: (2 * B * Hq * T * 4 + 255) // 256 * 256
+    # short sequences (bf16, d = 128): the work buffer + 128 KiB per chunk of
+    # the row-split dK/dV, at most 256 + B * Hkv * ceil(T / 128) chunks
+    for (B, T, Hq, Hkv) in ((1, 4096, 16, 2), (1, 1000, 8, 1), (2, 700, 12, 2), (1, 16384, 16, 2), (1, 257, 64, 1)):
+        n = lib.moda_bwd_workspace_bytes(B, T, Hq, Hkv, 128, 1)
+        extra = n - work(B, T, Hq)
+        assert extra > 0 and extra % (131072 * B * Hkv) == 0, (B, T, Hq, Hkv, n)
+        assert extra // 131072 <= 256 + B * Hkv * ((T + 127) // 128)
+    # no split: grids that fill the GPU, one key tile, generic kernels
+    for (B, T, Hq, Hkv, d, dt) in ((1, 65536, 16, 2, 128, 1), (2, 16384, 16, 2, 128, 1), (1, 100, 8, 1, 128, 1),
+                                   (1, 4096, 16, 2, 128, 0), (1, 4096, 16, 2, 64, 1)):
+        assert lib.moda_bwd_workspace_bytes(B, T, Hq, Hkv, d, dt) == work(B, T, Hq)
+    assert lib.moda_bwd_workspace_bytes(1, 4096, 16, 3, 128, 1) == -1     # Hq not a multiple of Hkv
+    assert lib.moda_bwd_workspace_bytes(1, 4096, 16, 2, 128, 9) == -1     # unknown dtype
+    need = lib.moda_bwd_workspace_bytes(1, 4096, 16, 2, 128, 1)
+    a = [FAKE] * 11 + [None, None, 1, 4096, 16, 2, 128, 0, 1]
+    assert lib.moda_bwd_ws(*a, None, need, None) == _lib.MODA_ERR_WORKSPACE              # no workspace
+    assert lib.moda_bwd_ws(*a, 4096, need - 1, None) == _lib.MODA_ERR_WORKSPACE          # too small
+    assert lib.moda_bwd_ws(*a, 4096 + 64, need, None) == _lib.MODA_ERR_WORKSPACE         # misaligned
+    a[15] = 3                                                                          # Hq % Hkv != 0
+    assert lib.moda_bwd_ws(*a, 4096, need, None) == _lib.MODA_ERR_SHAPE
