@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the write-step and depth-window measurements")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--bwd-ws", action="store_true",
+                    help="time the backward through moda_bwd_ws (row-split dK/dV on short sequences)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the depth-overhead sweep over the other bf16 workloads")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -512,6 +514,29 @@ def main():
                                           "ws_fwd_tflops": Fs / (t_w * 1e-3) / 1e12,
                                           "ws_overhead_vs_L0": t_w / t_w0 - 1.0})
                 del wk
+            if not args.no_bwd and sT <= 16384:
+                # the backward of this workload: moda_bwd, and moda_bwd_ws
+                # where it splits the dK/dV rows (short sequences)
+                sdo = rn(sB, sT, sHq, sd)
+                moda.moda_fwd(sq, sk, sv, skp, svp, sL, out=so, lse=sl)
+                sg = moda.moda_bwd(sq, sk, sv, skp, svp, sL, so, sl, sdo)
+                swk = torch.empty(2, sB, sHq, sT, dtype=torch.float32, device=dev)
+                fns = [lambda: moda.moda_bwd(sq, sk, sv, skp, svp, sL, so, sl, sdo, grads=sg, work=swk)]
+                split = moda.bwd_workspace_bytes(sB, sT, sHq, sHkv, sd, sq.dtype) > swk.numel() * 4 + 255
+                if split:
+                    bws = moda.bwd_workspace(sq, sk)
+                    fns.append(lambda: moda.moda_bwd(sq, sk, sv, skp, svp, sL, so, sl, sdo, grads=sg, workspace=bws))
+                for f in fns:
+                    f()
+                torch.cuda.synchronize()
+                tb = timed_launches(fns, 5)
+                sweep[ws["name"]]["bwd_ms"] = med(tb[0])
+                sweep[ws["name"]]["bwd_tflops"] = 2.5 * Fs / (med(tb[0]) * 1e-3) / 1e12
+                if split:
+                    sweep[ws["name"]]["ws_bwd_ms"] = med(tb[1])
+                    sweep[ws["name"]]["ws_bwd_tflops"] = 2.5 * Fs / (med(tb[1]) * 1e-3) / 1e12
+                    del bws
+                del sdo, sg, swk
             del sq, sk, sv, skd, svd, skp, svp, so, sl
         res["overhead_sweep"] = sweep
 
@@ -559,16 +584,17 @@ def main():
     if not args.no_bwd:
         # backward of the same forward: dq, dk/dv of sequence and depth keys
         from moda_inputs import make_dout
-        log("timing the backward (moda_bwd)")
+        log("timing the backward (" + ("moda_bwd_ws" if args.bwd_ws else "moda_bwd") + ")")
         moda.moda_fwd(q, ks, vs, kp, vp, L_d, out=out, lse=lse)
         dout = make_dout(B, T, Hq, d, dtype=w["dtype"], seed=w["seed"]).to(q.device)
-        grads = moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout)
+        bws = moda.bwd_workspace(q, ks) if args.bwd_ws else None
+        grads = moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout, workspace=bws)
         torch.cuda.synchronize()
         reps = 3
         eb = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         eb[0].record()
         for i in range(reps):
-            moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout, grads=grads)
+            moda.moda_bwd(q, ks, vs, kp, vp, L_d, out, lse, dout, grads=grads, workspace=bws)
             eb[i + 1].record()
         torch.cuda.synchronize()
         bwd_ms = sum(eb[i].elapsed_time(eb[i + 1]) for i in range(reps)) / reps
@@ -576,10 +602,11 @@ def main():
         # dP, dV, dQ, dK), 2.5x the forward's two; the kernels execute seven
         # (S and dP are formed once for dq and once for dk/dv)
         res["bwd_ms"] = bwd_ms
+        res["bwd_entry"] = "moda_bwd_ws" if args.bwd_ws else "moda_bwd"
         res["bwd_tflops"] = 2.5 * F / (bwd_ms * 1e-3) / 1e12
         res["bwd_frac_mfma_peak"] = res["bwd_tflops"] / peak
         log(f"bwd {bwd_ms:.3f} ms  {res['bwd_tflops']:.1f} TFLOP/s")
-        del grads, dout
+        del grads, dout, bws
 
     if not args.no_cpu_baseline:
         log(f"oracle on host cores ({args.cpu_budget:.0f} s budget)")
