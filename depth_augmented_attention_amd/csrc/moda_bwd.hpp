@@ -1170,6 +1170,9 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   const float lse2 = row_ok ? p.lse[lrow] * kLog2e : INFINITY;
   const float dlt = row_ok ? -p.work[lrow] : 0.f;
   const float sl2 = p.scale_log2;
+  f32x16 dp0;                                   // dP accumulators start at -Delta
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp0[r] = -dlt;
 
   f32x16 acc[NDT];
 #pragma unroll
@@ -1223,7 +1226,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
           ka[kc] = *reinterpret_cast<const bf16x8*>(sb + H * 32 * 256 + roff[kc]);
           va[kc] = *reinterpret_cast<const bf16x8*>(sb + OFF_V + H * 32 * 256 + roff[kc]);
         }
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{}, dp = dp0;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
           s = mma16(ka[kc], qf[kc], s);
@@ -1243,7 +1246,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = __builtin_amdgcn_exp2f(x[r]);
-          dsf[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dlt));
+          dsf[r >> 3][r & 7] = (bf16)(pr * dp[r]);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
