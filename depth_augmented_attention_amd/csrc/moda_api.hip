@@ -378,14 +378,17 @@ int moda_pack_depth_q8(const void* k_depth, const void* v_depth, int8_t* k_q, in
   if ((long long)T * L_d > 0x7fffffffLL - 32) return MODA_ERR_SHAPE;
   moda::PackQ8Params p{k_depth, v_depth, k_q, v_q, k_scale, v_scale, B, T, Hkv, L_d, padded_depth_keys(T, L_d)};
   div_magic(L_d, &p.ld_magic, &p.ld_shift);
-  // (b, kv head) planes by blocks of rows; at most 65535 planes per launch
+  // blocks of rows x (b, kv head) planes, planes fastest; launches of at most
+  // 2^31 - 1 workgroups
   const long long rpb = 2 * (256 / (d / moda::kQ8Elems));     // two rows per lane group
-  const long long gx = (p.NKp + rpb - 1) / rpb;
+  const long long nrb = (p.NKp + rpb - 1) / rpb;
   const long long planes = (long long)B * Hkv;
+  if (planes > 0x7fffffffLL) return MODA_ERR_SHAPE;
+  const long long per = 0x7fffffffLL / planes;                  // row blocks per launch
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  for (long long bh0 = 0; bh0 < planes; bh0 += 65535) {
-    p.bh0 = (int)bh0;
-    const dim3 grid((unsigned)gx, (unsigned)(planes - bh0 < 65535 ? planes - bh0 : 65535));
+  for (long long rb0 = 0; rb0 < nrb; rb0 += per) {
+    p.rb0 = rb0;
+    const dim3 grid((unsigned)((nrb - rb0 < per ? nrb - rb0 : per) * planes));
     if (dtype == MODA_BF16) {
       if (d == 128) hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 128>), grid, dim3(256), 0, s, p);
       else hipLaunchKernelGGL((moda::moda_pack_depth_q8_kernel<moda::bf16, 64>), grid, dim3(256), 0, s, p);

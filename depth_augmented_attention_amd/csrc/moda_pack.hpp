@@ -11,8 +11,10 @@
 //   k_packed [B][Hkv][NKp][D]   rows of d elements
 //   v_packed [B][Hkv][NKp][D]   the same for the values
 // with zero rows for n >= T * L_d (NKp = T * L_d rounded up to 32).  One
-// thread per 16-byte chunk of a packed row; reads and writes are contiguous
-// 16-byte accesses.
+// thread per 16-byte chunk, taken in the source order, so that consecutive
+// threads read consecutive bytes of both kv heads' rows; each (b, kv head)
+// destination then receives whole 256-byte rows (d = 128, bf16).  The threads
+// past the source chunks write the zero rows.
 #pragma once
 
 #include "moda_common.hpp"
@@ -33,22 +35,34 @@ __global__ __launch_bounds__(256) void moda_pack_depth_kernel(PackParams p) {
   constexpr int VE = Traits<E>::VE;
   constexpr int CPR = D / VE;                   // 16-byte chunks per row
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long rows = (long long)p.B * p.Hkv * p.NKp;
-  if (idx >= rows * CPR) return;
-  const long long row = idx / CPR;              // (bh, n) in packed order
-  const int c = (int)(idx % CPR);
-  const long long bh = row / p.NKp;
-  const int n = (int)(row % p.NKp);             // T * L_d < 2^31 (checked at the boundary)
-  const int b = (int)(bh / p.Hkv), kvh = (int)(bh % p.Hkv);
-  u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-  if (n < p.T * p.L_d) {
-    const int t = n / p.L_d, j = n - t * p.L_d;
-    const long long src = ((((long long)b * p.T + t) * p.L_d + j) * p.Hkv + kvh) * D + c * VE;
-    kv = ld16(reinterpret_cast<const E*>(p.kd) + src);
-    vv = ld16(reinterpret_cast<const E*>(p.vd) + src);
+  const long long TL = (long long)p.T * p.L_d;
+  const long long nsrc = (long long)p.B * TL * p.Hkv * CPR;
+  if (idx < nsrc) {
+    // source order: consecutive threads read consecutive bytes of [B,T,L_d,Hkv,d]
+    const long long rs = idx / CPR;
+    const int c = (int)(idx % CPR);
+    const long long r1 = rs / p.Hkv;
+    const int kvh = (int)(rs % p.Hkv);
+    const long long b = r1 / TL, n = r1 % TL;
+    const long long dst = ((b * p.Hkv + kvh) * p.NKp + n) * D + c * VE;
+    const u32x4 kv = ld16(reinterpret_cast<const E*>(p.kd) + rs * D + c * VE);
+    const u32x4 vv = ld16(reinterpret_cast<const E*>(p.vd) + rs * D + c * VE);
+    st16(reinterpret_cast<E*>(p.kp) + dst, kv);
+    st16(reinterpret_cast<E*>(p.vp) + dst, vv);
+    return;
   }
-  st16(reinterpret_cast<E*>(p.kp) + row * D + c * VE, kv);
-  st16(reinterpret_cast<E*>(p.vp) + row * D + c * VE, vv);
+  // zero rows n in [T L_d, NKp) of every (b, kv head)
+  const int npad = (int)(p.NKp - TL);
+  if (npad == 0) return;
+  const long long k = idx - nsrc;
+  const long long pr = k / CPR;
+  const int c = (int)(k % CPR);
+  const long long bh = pr / npad;
+  if (bh >= (long long)p.B * p.Hkv) return;
+  const long long dst = (bh * p.NKp + TL + pr % npad) * D + c * VE;
+  const u32x4 z = {0, 0, 0, 0};
+  st16(reinterpret_cast<E*>(p.kp) + dst, z);
+  st16(reinterpret_cast<E*>(p.vp) + dst, z);
 }
 
 }  // namespace moda
@@ -118,7 +132,7 @@ struct PackQ8Params {
   long long NKp;
   uint32_t ld_magic;  // n / L_d == (n * ld_magic) >> ld_shift for 0 <= n < 2^31
   int ld_shift;
-  int bh0;            // first (b, kv head) plane of this launch
+  long long rb0;      // first block of rows of this launch
 };
 
 constexpr int kQ8Elems = 16;   // elements per lane
@@ -230,7 +244,11 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p) {
   constexpr int LPR = D / kQ8Elems;             // lanes per packed row
   constexpr int RPB = 256 / LPR;                // rows per workgroup and pass
-  const int bh = p.bh0 + (int)blockIdx.y;       // (b, kv head) plane
+  // consecutive workgroups: the same rows of consecutive (b, kv head) planes,
+  // so that together they read consecutive bytes of [B, T, L_d, Hkv, d]
+  const int planes = p.B * p.Hkv;
+  const int bh = (int)(blockIdx.x % planes);    // (b, kv head) plane
+  const long long rblk = p.rb0 + blockIdx.x / planes;   // block of 2 * RPB packed rows
   const int l = threadIdx.x % LPR;
   const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
   float xk[2][kQ8Elems], xv[2][kQ8Elems];
@@ -238,8 +256,9 @@ __global__ __launch_bounds__(256) void moda_pack_depth_q8_kernel(PackQ8Params p)
   long long dst[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int n = ((int)blockIdx.x * 2 + u) * RPB + (int)threadIdx.x / LPR;   // packed row in the plane
-    in_plane[u] = n < p.NKp;
+    const long long nl = (rblk * 2 + u) * RPB + (int)threadIdx.x / LPR;   // packed row in the plane
+    in_plane[u] = nl < p.NKp;
+    const int n = in_plane[u] ? (int)nl : 0;
     dst[u] = (long long)bh * p.NKp + (in_plane[u] ? n : 0);
 #pragma unroll
     for (int j = 0; j < kQ8Elems; ++j) { xk[u][j] = 0.f; xv[u][j] = 0.f; }
