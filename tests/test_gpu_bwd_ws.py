@@ -67,6 +67,9 @@ CASES = [
     ("bf16_B3_T333_G5_L2", "bf16", 3, 333, 10, 2, 128, 2, True),
     ("bf16_T300_G16_L5", "bf16", 1, 300, 16, 1, 128, 5, True),
     ("bf16_T200_G8_L2", "bf16", 1, 200, 8, 1, 128, 2, True),        # two key tiles
+    ("bf16_T1025_G8_L4", "bf16", 1, 1025, 8, 1, 128, 4, True),      # last key tile one key long
+    ("bf16_B2_T1500_G2_L3", "bf16", 2, 1500, 4, 2, 128, 3, True),
+    ("bf16_T3000_G8_L6", "bf16", 1, 3000, 24, 3, 128, 6, True),     # three kv heads, ragged tail
     ("bf16_T512_G2_L3", "bf16", 1, 512, 8, 4, 128, 3, False),       # 16 query blocks: too few to cut
     ("bf16_T100_G8_L3", "bf16", 1, 100, 8, 1, 128, 3, False),       # one key tile
     ("fp32_T200_G4_d64_L2", "fp32", 1, 200, 4, 1, 64, 2, False),    # generic kernels: as moda_bwd
