@@ -1113,6 +1113,94 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_reduce_kernel(BwdParams p) 
 // as moda_bwd_dq_kernel): K and V blocks of 64 keys go straight into two LDS
 // stages; one swizzled copy of K serves the row-major score operand and, via
 // transpose reads, the K^T operand of dQ^T += K^T dS^T.
+// The depth slots' share of dQ for the bf16 d = 128 kernel: as dq_depth_fold,
+// with the key-transposed operand of dQ^T += K^T dS^T read from LDS.  The key
+// rows loaded for the score products go to this wave's 8 KB region of the
+// free LDS stages (swizzled like a sequence K block, unread slots as zero
+// rows), to be read back with the transpose reads of the sequence sweep --
+// instead of gathering 64 single elements per lane from memory.
+template <int D>
+__device__ __forceinline__ void dq_depth_fold_bf16(const BwdParams& p, int bh, int tw_min, int tw_max, int t_row,
+                                                   int n, int hh, int key_row, const bf16x8 (&qf)[D / 16],
+                                                   const bf16x8 (&df)[D / 16], float lse2, float dlt,
+                                                   f32x16 (&acc)[D / 32], char* region,
+                                                   const uint32_t (&tro)[8]) {
+  using namespace bwdbf16;
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32;
+  const float sl2 = p.scale_log2;
+  const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
+  const long long nlo = (long long)tw_min * L_cap + slot_lo;
+  const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
+  const bf16* kdb = reinterpret_cast<const bf16*>(p.kd) + (long long)bh * p.NKp * D;
+  const bf16* vdb = reinterpret_cast<const bf16*>(p.vd) + (long long)bh * p.NKp * D;
+  const int8_t* kq8 = reinterpret_cast<const int8_t*>(p.kd) + (long long)bh * p.NKp * D;
+  const int8_t* vq8 = reinterpret_cast<const int8_t*>(p.vd) + (long long)bh * p.NKp * D;
+  const float* ks8 = p.q8 ? p.ksc + (long long)bh * p.NKp : nullptr;
+  const float* vs8 = p.q8 ? p.vsc + (long long)bh * p.NKp : nullptr;
+  const int sw = swz(key_row);
+  for (long long n0 = nlo & ~31LL; n0 < nhi; n0 += 32) {
+    if (!depth_tile_used(n0, L_cap, slot_lo, L_d)) continue;
+    bf16x8 kf[NKC];
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const long long kr = n0 + key_row;
+    if (p.q8) {
+      const float ks = ks8[kr], vs = vs8[kr];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        kf[kc] = Dequant<bf16>::frag(kq8 + kr * D + hh * 8 + kc * 16, ks);
+        s = mma16(kf[kc], qf[kc], s);
+        dp = mma16(Dequant<bf16>::frag(vq8 + kr * D + hh * 8 + kc * 16, vs), df[kc], dp);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        kf[kc] = load_frag(kdb + kr * D + hh * 8 + kc * 16);
+        s = mma16(kf[kc], qf[kc], s);
+        dp = mma16(load_frag(vdb + kr * D + hh * 8 + kc * 16), df[kc], dp);
+      }
+    }
+    const long long own_lo = (long long)t_row * L_cap + slot_lo - n0;
+    const long long own_hi = own_lo + L_d;
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = reg_key(r, hh);
+      const bool own = key >= own_lo && key < own_hi;
+      const float pr = __builtin_amdgcn_exp2f(own ? s[r] * sl2 - lse2 : -INFINITY);
+      // a masked key contributes exactly 0 (its dP may be non-finite when the
+      // slot is unread)
+      ds[r] = own ? pr * (dp[r] - dlt) : 0.f;
+    }
+    // this lane's key row into the region (row key_row, 16-byte chunks
+    // 2 kc + hh); keys of unread slots (and padding) as zero rows: their dS is
+    // 0, and 0 * x would still carry a non-finite x into dQ
+    const uint32_t rows_ok = depth_tile_partial(n0, L_cap, slot_lo, L_d, p.T)
+                                 ? depth_tile_rows(n0, L_cap, slot_lo, L_d, p.T, n + 32 * hh) : 0xffffffffu;
+    const bool row_ok = (rows_ok >> key_row) & 1u;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(&kf[kc]) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(region + key_row * 256 + (((2 * kc + hh) ^ sw) * 16)) = v;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = (bf16)ds[c * 8 + j];
+      const char* kb = region + c * 16 * 256;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + tro[2 * dt]));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + tro[2 * dt + 1]));
+        const s16x4 pr[2] = {r0, r1};
+        acc[dt] = mma16(*reinterpret_cast<const bf16x8*>(pr), f, acc[dt]);
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moda_bwd_dq_bf16_kernel(BwdParams p) {
@@ -1279,7 +1367,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   if (j < nblocks) block.template operator()<0>(j);
 
   if (wave_active && p.L_d > 0)
-    dq_depth_fold<bf16, D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc);
+    dq_depth_fold_bf16<D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc, smem0 + wave * 8192, tro);
   if (row_ok) dq_store<bf16, D>(p, b, t_row, hq, hh, acc);
 }
 
