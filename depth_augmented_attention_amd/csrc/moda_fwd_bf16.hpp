@@ -44,11 +44,16 @@
 //     twice the key blocks of the average one, and on a small grid it alone
 //     sets the time.  With a workspace, each of the nsplit longest tiles of a
 //     (b, kv head) -- tile i, paired with the short tile j = ntiles - 1 - i --
-//     is swept by two workgroups: part 0 over key blocks [0, h), part 1 over
-//     [h, nb_i) plus the depth slots, h = (nb_i - nb_j) / 2.  Parts run
+//     is swept by two workgroups: part 0 over key blocks [0, h) plus the
+//     depth slots, part 1 over [h, nb_i), h = (nb_i - nb_j) / 2.  Parts run
 //     first, then the short tiles longest first; a compute unit whose part 0
 //     ends early takes the next short tile, so part 0 + short tile and part 1
-//     each come to about (nb_i + nb_j) / 2 blocks.  Each wave of a part writes
+//     each come to about (nb_i + nb_j) / 2 blocks.  The depth fold goes with
+//     part 0 because parts 0 end at spread-out times (h varies with the tile)
+//     while parts 1 all end together: folded at the end of part 1, every
+//     compute unit would fetch its depth slots at once, at the end of the
+//     kernel, bound by HBM; spread out, each fold runs beside another
+//     workgroup's sweep.  Each wave of a part writes
 //     its running state (O, m, l per lane) to the workspace, and the second
 //     wave of the pair to arrive (a device-wide counter) merges the other's
 //     state into its own -- m = max(m0, m1), O = 2^(m0 - m) O0 + 2^(m1 - m) O1,
@@ -433,7 +438,7 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   }
 
   // ---- depth fold: this wave's positions only (see moda_fwd.hpp) ----
-  if (wave_active && p.L_d > 0 && part != 0) {
+  if (wave_active && p.L_d > 0 && part != 1) {
     const int L_d = p.L_d, L_cap = p.L_cap, slot_lo = p.slot_lo;
     const long long nlo = (long long)tw_min * L_cap + slot_lo;
     const long long nhi = (long long)tw_max * L_cap + slot_lo + L_d;
