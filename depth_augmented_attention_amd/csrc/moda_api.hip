@@ -4,6 +4,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "moda.h"
@@ -258,6 +259,35 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
+// Launch counters of the eight-wave forward grids (work items drawn in the
+// order workgroups start): a ring of slots in a file-scope device array, one
+// copy per GPU, zero at load; each launch takes the next slot and leaves it
+// at zero when it ends, so launches in flight at the same time on one GPU
+// (other streams) use different slots as long as fewer than kTickSlots of them
+// overlap.  The per-device address comes from hipGetSymbolAddress, once per
+// device; without it the grid keeps the blockIdx order.
+constexpr int kTickSlots = 1024;
+static __device__ __align__(256) uint32_t fwd_tick[2 * kTickSlots];
+static std::mutex g_tick_mu;
+static uint32_t* g_tick_ptr[64] = {};
+static std::atomic<uint32_t> g_tick_next{0};
+
+static uint32_t* fwd_tick_slot() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  uint32_t* base;
+  {
+    std::lock_guard<std::mutex> lock(g_tick_mu);
+    if (!g_tick_ptr[dev]) {
+      void* a = nullptr;
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(fwd_tick)) != hipSuccess || !a) return nullptr;
+      g_tick_ptr[dev] = static_cast<uint32_t*>(a);
+    }
+    base = g_tick_ptr[dev];
+  }
+  return base + 2 * (g_tick_next.fetch_add(1, std::memory_order_relaxed) % kTickSlots);
+}
+
 static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
                     const void* v_depth, const float* k_scale, const float* v_scale, int q8, void* out,
                     float* lse, int B, int T, int Hq, int Hkv, int d, int L_cap, int slot_lo, int slot_hi,
@@ -308,6 +338,9 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
     }
   }
   if (ks && p.nsplit == 0) nw = -8;   // (launch_fwd: the key-split instantiation)
+  p.tick = nullptr;
+  if (dtype == MODA_BF16 && d == 128 && nw == 8 && launch_grid > kCUs && launch_grid * 8 < 0xffffffffLL)
+    p.tick = fwd_tick_slot();
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

@@ -56,6 +56,10 @@ struct FwdParams {
   int nsplit;       // split tiles per (b, kvh); 0: every tile is whole
   float* ws;        // [BH * nsplit][2 parts][NW waves][66][64] float32 partial states
   uint32_t* cnt;    // [BH * nsplit][NW] arrival counters
+  // eight-wave grids of several rounds: this launch's counter slot,
+  // [work items taken, waves done], zero before and after the launch; null:
+  // work items in blockIdx order
+  uint32_t* tick;
 };
 
 // Whether the 32 packed depth keys [n0, n0 + 32) hold any slot of the window

@@ -147,8 +147,29 @@ void moda_fwd_bf16_kernel(FwdParams p) {
   const int rw = KS ? (wave & 3) : wave;  // row group of the tile
   const int kh = KS ? (wave >> 2) : 0;    // key half (stage set) of the wave
 
+  // Work item of this workgroup.  Eight-wave grids of several rounds take
+  // it from a launch counter in the order workgroups start (the longest
+  // tiles still first), not from blockIdx: the GPU hands workgroups to its
+  // eight XCDs round-robin by blockIdx, and XCDs run at different speeds
+  // (on one MI355X the odd ones took 3.5% longer over the same tiles), so a
+  // fixed split of the grid leaves the fast XCDs idle while the slow ones
+  // finish; drawn from the counter, each XCD takes work while it has time.
+  constexpr bool DYN = NW == 8 && !KS && !SPLIT;
+  uint32_t wg = blockIdx.x;
+  if constexpr (DYN) {
+    if (p.tick) {
+      __shared__ uint32_t s_wg;
+      if (tid == 0) s_wg = __hip_atomic_fetch_add(p.tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      wg = s_wg;
+    }
+  }
+
   const int BH = p.B * p.Hkv;
-  const int bh = blockIdx.x % BH;
+  // counter order: one (b, kv head) after another, so that the workgroups
+  // running at one time share the K/V blocks of one head in each XCD's L2
+  // (with blockIdx order each XCD keeps to one head by itself)
+  const int bh = DYN && p.tick ? (int)(wg / (uint32_t)p.ntiles) : (int)(wg % (uint32_t)BH);
   // part 0 / 1 of a split tile, or -1 for a whole tile
   int tile, part = -1;
   if constexpr (SPLIT) {
@@ -159,8 +180,10 @@ void moda_fwd_bf16_kernel(FwdParams p) {
     } else {
       tile = p.ntiles - 1 - H - (slot - 2 * H);
     }
+  } else if (DYN && p.tick) {
+    tile = p.ntiles - 1 - (int)(wg % (uint32_t)p.ntiles);
   } else {
-    tile = query_tile((int)(blockIdx.x / BH), p.ntiles, p.paired);
+    tile = query_tile((int)(wg / (uint32_t)BH), p.ntiles, p.paired);
   }
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
@@ -648,6 +671,18 @@ void moda_fwd_bf16_kernel(FwdParams p) {
                o[dt][g4 * 4 + 2] * inv, o[dt][g4 * 4 + 3] * inv);
     if (hh_out == 0 && p.lse)
       p.lse[((long long)b * p.Hq + h_out) * T + t_out] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  }
+  if constexpr (DYN) {
+    // every wave counts itself out; the last of the launch returns the
+    // counter slot to zero for the next launch that draws it (every
+    // workgroup has taken its work item before any of its waves gets here)
+    if (p.tick && lane == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(p.tick + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == gridDim.x * (uint32_t)NW - 1u) {
+        __hip_atomic_store(p.tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.tick + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 

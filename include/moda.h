@@ -114,6 +114,15 @@ int moda_pack_depth(const void* k_depth, const void* v_depth,
  * Scores are computed with float32 accumulation; softmax statistics and the
  * output accumulator are float32.  With L_d == 0 the call is causal GQA
  * attention, run by the same kernel.  out must not overlap any input.
+ *
+ * Grids of several rounds (bf16, d = 128, at least 131072 query rows
+ * B * T * Hq) hand out their query tiles through a launch counter, so that
+ * faster parts of the GPU take more tiles: the library keeps a ring of 1024
+ * such counters per GPU in its own device memory (8 KiB, nothing allocated
+ * per call), one per launch, each back at zero when its launch ends.  Up to
+ * 1024 of these forward launches (this call, moda_fwd_window and the 8-bit
+ * variants) may run at the same time on one GPU, on any streams; results
+ * do not depend on the order in which tiles are taken.
  */
 int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
              const void* k_depth, const void* v_depth,

@@ -176,3 +176,40 @@ def test_errors_raise():
         moda.moda_fwd(q, k, k, None, None, 0, out=torch.empty(1, 2, 2, 128, dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):                    # caller's out of another dtype
         moda.moda_fwd(q, k, k, None, None, 0, out=torch.empty(1, 4, 2, 128, dtype=torch.float32, device="cuda"))
+
+
+def test_counter_order_repeatable_and_concurrent():
+    """Grids of several rounds take their query tiles from a per-launch
+    counter slot that each launch returns to zero: calls in a row, and calls
+    in flight at the same time on two streams, give bit-identical results
+    (a slot left non-zero would make the next launch skip tiles), equal to
+    the oracle on sampled rows."""
+    B, T, Hq, Hkv, d, L = 1, 16384, 16, 2, 128, 4
+    _say(f"counter order: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L} (8-wave grid, 4 rounds)")
+    inputs = make_inputs(B, T, Hq, Hkv, d, L, dtype="bf16", seed=4242)
+    dev = torch.device("cuda:0")
+    q, ks, vs, kd, vd = [x.to(dev) for x in inputs]
+    kp = torch.empty(moda.depth_packed_elems(B, T, Hkv, d, L), dtype=q.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    moda.moda_pack_depth(kd, vd, kp, vp)
+    outs = []
+    for _ in range(3):
+        o, l = moda.moda_fwd(q, ks, vs, kp, vp, L)
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    conc = []
+    for _ in range(2):
+        for s in (s1, s2):
+            o = torch.empty_like(q)
+            l = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                moda.moda_fwd(q, ks, vs, kp, vp, L, out=o, lse=l, stream=s)
+            conc.append((o, l))
+    torch.cuda.synchronize()
+    o0, l0 = outs[0]
+    for i, (o, l) in enumerate(outs[1:] + conc):
+        assert torch.equal(o, o0) and torch.equal(l, l0), f"call {i + 1} differs from the first"
+    rows = sample_rows(B, T, Hq, n=512, seed=4243, tile_rows=(T - 1,))
+    _check("counter order", inputs[0].dtype, *compare_rows(inputs, o0.cpu(), l0.cpu(), rows))
