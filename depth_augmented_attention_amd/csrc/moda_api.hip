@@ -259,20 +259,21 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
   return e == hipSuccess ? MODA_OK : MODA_ERR_HIP;
 }
 
-// Launch counters of the eight-wave forward grids (work items drawn in the
-// order workgroups start): a ring of slots in a file-scope device array, one
-// copy per GPU, zero at load; each launch takes the next slot and leaves it
-// at zero when it ends, so launches in flight at the same time on one GPU
-// (other streams) use different slots as long as fewer than kTickSlots of them
+// Launch counters of the grids of several rounds (the eight-wave forward,
+// the backward's dQ and dK/dV kernels: work items drawn in the order
+// workgroups start): a ring of slots in a file-scope device array, one copy
+// per GPU, zero at load; each launch takes the next slot and leaves it at
+// zero when it ends, so launches in flight at the same time on one GPU (other
+// streams) use different slots as long as fewer than kTickSlots of them
 // overlap.  The per-device address comes from hipGetSymbolAddress, once per
-// device; without it the grid keeps the blockIdx order.
+// device; without it a grid keeps the blockIdx order.
 constexpr int kTickSlots = 1024;
-static __device__ __align__(256) uint32_t fwd_tick[2 * kTickSlots];
+static __device__ __align__(256) uint32_t work_tick[2 * kTickSlots];
 static std::mutex g_tick_mu;
 static uint32_t* g_tick_ptr[64] = {};
 static std::atomic<uint32_t> g_tick_next{0};
 
-static uint32_t* fwd_tick_slot() {
+static uint32_t* tick_slot() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   uint32_t* base;
@@ -280,7 +281,7 @@ static uint32_t* fwd_tick_slot() {
     std::lock_guard<std::mutex> lock(g_tick_mu);
     if (!g_tick_ptr[dev]) {
       void* a = nullptr;
-      if (hipGetSymbolAddress(&a, HIP_SYMBOL(fwd_tick)) != hipSuccess || !a) return nullptr;
+      if (hipGetSymbolAddress(&a, HIP_SYMBOL(work_tick)) != hipSuccess || !a) return nullptr;
       g_tick_ptr[dev] = static_cast<uint32_t*>(a);
     }
     base = g_tick_ptr[dev];
@@ -340,7 +341,7 @@ static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   if (ks && p.nsplit == 0) nw = -8;   // (launch_fwd: the key-split instantiation)
   p.tick = nullptr;
   if (dtype == MODA_BF16 && d == 128 && nw == 8 && launch_grid > kCUs && launch_grid * 8 < 0xffffffffLL)
-    p.tick = fwd_tick_slot();
+    p.tick = tick_slot();
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
@@ -570,6 +571,20 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.kchunk = split.C;
   p.kfull = split.full;
   p.kitems = split.items;
+  // grids of several rounds take their work items from a launch counter:
+  // dQ (two workgroups per compute unit) and the unsplit bf16 dK/dV kernel
+  // (one per compute unit).  Only with at most two (b, kv head) pairs: the
+  // counter spreads every pair over every XCD, and each dK/dV workgroup
+  // streams its pair's q / dO rows, so with more pairs each XCD's L2 serves
+  // more streams (B = 2, Hkv = 2: +2.5% with the counter; B = 1, Hkv = 2,
+  // T = 64K: -1.4%)
+  p.tick_dq = p.tick_kv = nullptr;
+  if (dtype == MODA_BF16 && d == 128 && (long long)B * Hkv <= 2) {
+    const long long gq = (long long)B * Hkv * ntiles, gk = (long long)B * Hkv * nktiles;
+    if (gq > 2 * kCUs && gq * 4 < 0xffffffffLL) p.tick_dq = tick_slot();
+    if (split.C == 0 && dkdv_form(dtype, d, T, G, Hq) != DkdvForm::generic && gk > kCUs && gk * 4 < 0xffffffffLL)
+      p.tick_kv = tick_slot();
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;

@@ -77,7 +77,34 @@ struct BwdParams {
   int kchunk;          // query blocks per chunk, a multiple of 2G; 0: no split
   int kfull;           // full chunks over all key tiles of one (b, kv head)
   int kitems;          // chunks (full and remainder) of one (b, kv head)
+  // grids of several rounds: the launch counter slots of the dQ and the
+  // (unsplit) dK/dV kernels, [work items taken, waves done], zero before and
+  // after each launch; null: work items in blockIdx order
+  uint32_t* tick_dq;
+  uint32_t* tick_kv;
 };
+
+// Work item of a workgroup: from the launch counter slot `tick` when there is
+// one (in the order workgroups start -- XCDs, which take workgroups
+// round-robin by blockIdx, run at different speeds, so a fixed split of the
+// grid leaves the fast ones idle at the end), else blockIdx.
+__device__ __forceinline__ uint32_t take_work_item(uint32_t* tick, uint32_t* s_item) {
+  if (!tick) return blockIdx.x;
+  if (threadIdx.x == 0) *s_item = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *s_item;
+}
+// Each wave counts itself out once its work is written; the last wave of
+// the launch returns the slot to zero (every workgroup has taken its item
+// before any of its waves gets here).
+__device__ __forceinline__ void release_work_slot(uint32_t* tick, int waves_per_group) {
+  if (!tick || (threadIdx.x & 63) != 0) return;
+  const uint32_t done = __hip_atomic_fetch_add(tick + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == gridDim.x * (uint32_t)waves_per_group - 1u) {
+    __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tick + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -767,19 +794,25 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int BH = p.B * p.Hkv;
-  const int bh = blockIdx.x % BH;
+  // work item from the launch counter or blockIdx, in the same order: key
+  // tiles across the (b, kv head) pairs, heaviest first (a grid of a few
+  // rounds needs that order to end with light tiles)
+  uint32_t* const tick = SPLIT ? nullptr : p.tick_kv;
+  __shared__ uint32_t s_item;
+  const uint32_t item = take_work_item(tick, &s_item);
+  const int bh = (int)(item % (uint32_t)BH);
   // SPLIT: blocks [q_lo, q_hi) of the tile's sweep (chunks of the row-split
   // map); otherwise every block, the earliest keys (most rows) first
-  int ktile = (int)(blockIdx.x / BH), q_lo = 0, q_hi = 0, nchunks = 1;
+  int ktile = (int)(item / (uint32_t)BH), q_lo = 0, q_hi = 0, nchunks = 1;
   if constexpr (SPLIT) {
     const BwdChunkMap cm(p.T, p.G, p.kchunk, p.nktiles);
-    const int item = ktile;
-    if (item < p.kfull) {
-      ktile = cm.full_tile(item);
-      q_lo = (item - cm.prefix(ktile)) * p.kchunk;
+    const int chunk = ktile;
+    if (chunk < p.kfull) {
+      ktile = cm.full_tile(chunk);
+      q_lo = (chunk - cm.prefix(ktile)) * p.kchunk;
       q_hi = q_lo + p.kchunk;
     } else {
-      ktile = cm.rem_tile(item - p.kfull);
+      ktile = cm.rem_tile(chunk - p.kfull);
       if (ktile < 0) return;                    // past the map (not launched)
       q_lo = cm.nf(ktile) * p.kchunk;
       q_hi = cm.nqb(ktile);
@@ -1057,6 +1090,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
         store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
       }
   }
+  release_work_slot(tick, NW);
 }
 
 // Row-split dK/dV: the sum of a key tile's partial sums, in chunk order (its
@@ -1227,8 +1261,11 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int BH = p.B * p.Hkv;
-  const int bh = blockIdx.x % BH;
-  const int tile = p.ntiles - 1 - (int)(blockIdx.x / BH);   // heaviest first
+  // work item from the launch counter or blockIdx: heaviest tiles first
+  __shared__ uint32_t s_item;
+  const uint32_t item = take_work_item(p.tick_dq, &s_item);
+  const int bh = (int)(item % (uint32_t)BH);
+  const int tile = p.ntiles - 1 - (int)(item / (uint32_t)BH);
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;
@@ -1369,6 +1406,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   if (wave_active && p.L_d > 0)
     dq_depth_fold_bf16<D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc, smem0 + wave * 8192, tro);
   if (row_ok) dq_store<bf16, D>(p, b, t_row, hq, hh, acc);
+  release_work_slot(p.tick_dq, NW);
 }
 
 // ---------------------------------------------------------------------------

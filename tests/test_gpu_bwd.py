@@ -208,3 +208,33 @@ def test_bwd_window_parity(case):
     got = [g.double().cpu().numpy() for g in grads]
     ref = moda_backward(np32(q), np32(ks), np32(vs), np32(kd)[:, :, lo:hi], np32(vd)[:, :, lo:hi], np32(dout))
     _check_all(f"window {case}", q.dtype, got, ref)
+
+
+def test_bwd_counter_order_repeatable_and_concurrent():
+    """With B * Hkv <= 2 the long dQ and dK/dV grids take their tiles from
+    per-launch counter slots that each launch returns to zero: backward calls
+    in a row, and calls in flight at the same time on two streams, give
+    bit-identical gradients (a slot left non-zero would make the next launch
+    skip tiles)."""
+    B, T, Hq, Hkv, d, L = 1, 32768, 16, 2, 128, 4
+    _say(f"bwd counter order: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L} (dQ 4096 and dK/dV 512 workgroups)")
+    dev = torch.device("cuda:0")
+    q, ks, vs, kd, vd = [x.to(dev) for x in make_inputs(B, T, Hq, Hkv, d, L, dtype="bf16", seed=5151)]
+    dout = make_dout(B, T, Hq, d, dtype="bf16", seed=5152).to(dev)
+    kp, vp = moda.moda_pack_depth(kd, vd)
+    out, lse = moda.moda_fwd(q, ks, vs, kp, vp, L)
+    ref = moda.moda_bwd(q, ks, vs, kp, vp, L, out, lse, dout)
+    runs = [moda.moda_bwd(q, ks, vs, kp, vp, L, out, lse, dout)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for s in (s1, s2):
+        g = tuple(torch.empty_like(x) for x in ref)
+        w = torch.empty(2, B, Hq, T, dtype=torch.float32, device=dev)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            moda.moda_bwd(q, ks, vs, kp, vp, L, out, lse, dout, grads=g, work=w, stream=s)
+        runs.append(g)
+    torch.cuda.synchronize()
+    for i, g in enumerate(runs):
+        for name, a, b in zip(NAMES, ref, g):
+            assert torch.equal(a, b), f"call {i + 1}: {name} differs from the first call"
