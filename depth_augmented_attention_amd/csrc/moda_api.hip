@@ -268,7 +268,7 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
 // overlap.  The per-device address comes from hipGetSymbolAddress, once per
 // device; without it a grid keeps the blockIdx order.
 constexpr int kTickSlots = 1024;
-static __device__ __align__(256) uint32_t work_tick[2 * kTickSlots];
+static __device__ __align__(256) uint32_t work_tick[moda::kTickWords * kTickSlots];
 static std::mutex g_tick_mu;
 static uint32_t* g_tick_ptr[64] = {};
 static std::atomic<uint32_t> g_tick_next{0};
@@ -286,7 +286,7 @@ static uint32_t* tick_slot() {
     }
     base = g_tick_ptr[dev];
   }
-  return base + 2 * (g_tick_next.fetch_add(1, std::memory_order_relaxed) % kTickSlots);
+  return base + moda::kTickWords * (g_tick_next.fetch_add(1, std::memory_order_relaxed) % kTickSlots);
 }
 
 static int fwd_impl(const void* q, const void* k_seq, const void* v_seq, const void* k_depth,
@@ -571,15 +571,12 @@ static int bwd_impl(const void* q, const void* k_seq, const void* v_seq, const v
   p.kchunk = split.C;
   p.kfull = split.full;
   p.kitems = split.items;
-  // grids of several rounds take their work items from a launch counter:
-  // dQ (two workgroups per compute unit) and the unsplit bf16 dK/dV kernel
-  // (one per compute unit).  Only with at most two (b, kv head) pairs: the
-  // counter spreads every pair over every XCD, and each dK/dV workgroup
-  // streams its pair's q / dO rows, so with more pairs each XCD's L2 serves
-  // more streams (B = 2, Hkv = 2: +2.5% with the counter; B = 1, Hkv = 2,
-  // T = 64K: -1.4%)
+  // grids of several rounds take their work items from launch counters
+  // (one queue per (b, kv head) pair, at most kTickWords - 1 pairs): dQ (two
+  // workgroups per compute unit) and the unsplit bf16 dK/dV kernel (one per
+  // compute unit)
   p.tick_dq = p.tick_kv = nullptr;
-  if (dtype == MODA_BF16 && d == 128 && (long long)B * Hkv <= 2) {
+  if (dtype == MODA_BF16 && d == 128 && (long long)B * Hkv <= moda::kTickWords - 1) {
     const long long gq = (long long)B * Hkv * ntiles, gk = (long long)B * Hkv * nktiles;
     if (gq > 2 * kCUs && gq * 4 < 0xffffffffLL) p.tick_dq = tick_slot();
     if (split.C == 0 && dkdv_form(dtype, d, T, G, Hq) != DkdvForm::generic && gk > kCUs && gk * 4 < 0xffffffffLL)

@@ -84,25 +84,47 @@ struct BwdParams {
   uint32_t* tick_kv;
 };
 
-// Work item of a workgroup: from the launch counter slot `tick` when there is
-// one (in the order workgroups start -- XCDs, which take workgroups
-// round-robin by blockIdx, run at different speeds, so a fixed split of the
-// grid leaves the fast ones idle at the end), else blockIdx.
-__device__ __forceinline__ uint32_t take_work_item(uint32_t* tick, uint32_t* s_item) {
-  if (!tick) return blockIdx.x;
-  if (threadIdx.x == 0) *s_item = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Work item of a workgroup, as (b, kv head) pair and index within that
+// pair's tiles (0 = heaviest).  With a launch counter slot `tick` (one queue
+// counter per pair, then the count of waves done): the workgroup takes the
+// next tile of its home pair blockIdx % npairs -- the pair that blockIdx
+// order would give it, so that each XCD (the GPU hands workgroups to its
+// eight XCDs round-robin by blockIdx) keeps to the q / dO rows of few pairs in
+// its L2 -- and once that pair's tiles are all taken, the next tile of the
+// following pairs.  XCDs run at different speeds, so a fixed split of the
+// grid leaves the fast ones idle at the end; here they take over the slow
+// ones' last tiles.  Every workgroup finds a tile: the grid has exactly one
+// workgroup per tile, so while one is still looking, some pair has a tile
+// left.  Without a slot: blockIdx order.
+struct WorkItem {
+  int pair, index;
+};
+__device__ __forceinline__ WorkItem take_work_item(uint32_t* tick, int npairs, int per_pair, uint32_t* s_item) {
+  if (!tick) return WorkItem{(int)(blockIdx.x % (uint32_t)npairs), (int)(blockIdx.x / (uint32_t)npairs)};
+  if (threadIdx.x == 0) {
+    int q = (int)(blockIdx.x % (uint32_t)npairs);
+    uint32_t it = 0;
+    for (int k = 0; k < npairs; ++k) {
+      it = __hip_atomic_fetch_add(tick + q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (it < (uint32_t)per_pair) break;
+      q = q + 1 == npairs ? 0 : q + 1;
+    }
+    *s_item = (uint32_t)q * (uint32_t)per_pair + it;
+  }
   __syncthreads();
-  return *s_item;
+  const uint32_t v = *s_item;
+  return WorkItem{(int)(v / (uint32_t)per_pair), (int)(v % (uint32_t)per_pair)};
 }
-// Each wave counts itself out once its work is written; the last wave of
-// the launch returns the slot to zero (every workgroup has taken its item
-// before any of its waves gets here).
-__device__ __forceinline__ void release_work_slot(uint32_t* tick, int waves_per_group) {
+// Each wave counts itself out once its work is written (in the slot's last
+// word); the last wave of the launch returns the slot to zero (every
+// workgroup has taken its tile before any of its waves gets here).
+constexpr int kTickWords = 16;   // words per counter slot: up to 15 pairs, then the count
+__device__ __forceinline__ void release_work_slot(uint32_t* tick, int npairs, int waves_per_group) {
   if (!tick || (threadIdx.x & 63) != 0) return;
-  const uint32_t done = __hip_atomic_fetch_add(tick + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t done = __hip_atomic_fetch_add(tick + kTickWords - 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (done == gridDim.x * (uint32_t)waves_per_group - 1u) {
-    __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(tick + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < npairs; ++q) __hip_atomic_store(tick + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tick + kTickWords - 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -794,16 +816,15 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int BH = p.B * p.Hkv;
-  // work item from the launch counter or blockIdx, in the same order: key
-  // tiles across the (b, kv head) pairs, heaviest first (a grid of a few
-  // rounds needs that order to end with light tiles)
+  // work item: key tiles of each (b, kv head) pair, earliest keys (most
+  // rows, the heaviest) first
   uint32_t* const tick = SPLIT ? nullptr : p.tick_kv;
   __shared__ uint32_t s_item;
-  const uint32_t item = take_work_item(tick, &s_item);
-  const int bh = (int)(item % (uint32_t)BH);
+  const WorkItem wi = take_work_item(tick, BH, SPLIT ? p.kitems : p.nktiles, &s_item);
+  const int bh = wi.pair;
   // SPLIT: blocks [q_lo, q_hi) of the tile's sweep (chunks of the row-split
-  // map); otherwise every block, the earliest keys (most rows) first
-  int ktile = (int)(item / (uint32_t)BH), q_lo = 0, q_hi = 0, nchunks = 1;
+  // map); otherwise every block
+  int ktile = wi.index, q_lo = 0, q_hi = 0, nchunks = 1;
   if constexpr (SPLIT) {
     const BwdChunkMap cm(p.T, p.G, p.kchunk, p.nktiles);
     const int chunk = ktile;
@@ -1090,7 +1111,7 @@ __global__ __launch_bounds__(256) void moda_bwd_dkdv_bf16_kernel(BwdParams p) {
         store4(dvp + e, dv[dt][g4 * 4 + 0], dv[dt][g4 * 4 + 1], dv[dt][g4 * 4 + 2], dv[dt][g4 * 4 + 3]);
       }
   }
-  release_work_slot(tick, NW);
+  release_work_slot(tick, BH, NW);
 }
 
 // Row-split dK/dV: the sum of a key tile's partial sums, in chunk order (its
@@ -1261,11 +1282,11 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   const int hh = lane >> 5;
 
   const int BH = p.B * p.Hkv;
-  // work item from the launch counter or blockIdx: heaviest tiles first
+  // work item: query tiles of each (b, kv head) pair, heaviest first
   __shared__ uint32_t s_item;
-  const uint32_t item = take_work_item(p.tick_dq, &s_item);
-  const int bh = (int)(item % (uint32_t)BH);
-  const int tile = p.ntiles - 1 - (int)(item / (uint32_t)BH);
+  const WorkItem wi = take_work_item(p.tick_dq, BH, p.ntiles, &s_item);
+  const int bh = wi.pair;
+  const int tile = p.ntiles - 1 - wi.index;
   const int b = bh / p.Hkv;
   const int kvh = bh % p.Hkv;
   const int G = p.G;
@@ -1406,7 +1427,7 @@ void moda_bwd_dq_bf16_kernel(BwdParams p) {
   if (wave_active && p.L_d > 0)
     dq_depth_fold_bf16<D>(p, bh, tw_min, tw_max, t_row, n, hh, key_row, qf, df, lse2, dlt, acc, smem0 + wave * 8192, tro);
   if (row_ok) dq_store<bf16, D>(p, b, t_row, hq, hh, acc);
-  release_work_slot(p.tick_dq, NW);
+  release_work_slot(p.tick_dq, BH, NW);
 }
 
 // ---------------------------------------------------------------------------

@@ -121,7 +121,7 @@ int moda_pack_depth(const void* k_depth, const void* v_depth,
  * such counters per GPU in its own device memory (8 KiB, nothing allocated
  * per call), one per launch, each back at zero when its launch ends.  Up to
  * 1024 launches that use them (this call, moda_fwd_window and the 8-bit
- * variants; the backward calls' long grids with B * Hkv <= 2) may run at the
+ * variants; the backward calls' long grids with B * Hkv <= 15) may run at the
  * same time on one GPU, on any streams; results do not depend on the order
  * in which tiles are taken.
  */
@@ -299,7 +299,7 @@ int moda_fwd_q8(const void* q, const void* k_seq, const void* v_seq,
  * Every output element is written (no accumulation into existing contents).
  * Products use float32 accumulation; P and dS enter them in dtype.  All
  * outputs must be distinct and must not overlap any input.  With bf16,
- * d = 128, B * Hkv <= 2 and grids of several rounds, the dQ and dK/dV
+ * d = 128, B * Hkv <= 15 and grids of several rounds, the dQ and dK/dV
  * kernels take their tiles from the launch counters described at moda_fwd
  * (no allocation; results independent of the order).
  */
