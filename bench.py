@@ -580,6 +580,37 @@ def main():
         res["gpu_sclk_mhz_under_load"] = cur
         res["gpu_sclk_mhz_max"] = top
         log(f"sclk under load {cur} MHz (max {top} MHz)")
+        # context for the pages' comparison with FlashAttention-2 (their
+        # kernel at 97.3% of its efficiency at 64K): PyTorch's own
+        # flash-attention backend on the same GPU, plain causal attention at
+        # this shape (K/V heads repeated to Hq), launches after the cache fill
+        # taken in turn with moda_fwd at L_d = 0; the flash backend only (no
+        # fallback to another backend)
+        try:
+            from torch.nn.attention import SDPBackend, sdpa_kernel
+            qt = q.transpose(1, 2).contiguous()
+            kt = ks.transpose(1, 2).repeat_interleave(Hq // Hkv, dim=1).contiguous()
+            vt = vs.transpose(1, 2).repeat_interleave(Hq // Hkv, dim=1).contiguous()
+
+            def sdpa():
+                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+            sdpa()
+            moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)
+            torch.cuda.synchronize()
+            ts, tm = timed_launches([sdpa, lambda: moda.moda_fwd(q, ks, vs, None, None, 0, out=out, lse=lse)], 5)
+            F0 = useful_flops(B, T, Hq, d, 0)
+            sd = {"backend": "torch SDPA, FLASH_ATTENTION", "ms_median": med(ts),
+                  "tflops": F0 / (med(ts) * 1e-3) / 1e12, "moda_fwd_L0_ms_median": med(tm),
+                  "moda_fwd_L0_tflops": F0 / (med(tm) * 1e-3) / 1e12}
+            # useful TFLOP/s of the timed MoDA forward (with its depth slots)
+            # over the library's plain causal attention
+            sd["moda_vs_sdpa_efficiency"] = res["fwd_tflops"] / sd["tflops"]
+            res["torch_sdpa_flash_L0"] = sd
+            del qt, kt, vt
+            log(f"torch SDPA flash (L_d = 0): {sd['ms_median']:.3f} ms, {sd['tflops']:.1f} TFLOP/s")
+        except Exception as e:      # backend missing on this build: recorded, not fatal
+            res["torch_sdpa_flash_L0"] = {"unavailable": f"{type(e).__name__}: {str(e)[:200]}"}
 
     if not args.no_bwd:
         # backward of the same forward: dq, dk/dv of sequence and depth keys
