@@ -123,7 +123,8 @@ int moda_pack_depth(const void* k_depth, const void* v_depth,
  * 1024 launches that use them (this call, moda_fwd_window and the 8-bit
  * variants; the backward calls' long grids with B * Hkv <= 15) may run at the
  * same time on one GPU, on any streams; results do not depend on the order
- * in which tiles are taken.
+ * in which tiles are taken.  A launch recorded into a HIP graph keeps the
+ * counter it was given: replays of one graph must not overlap each other.
  */
 int moda_fwd(const void* q, const void* k_seq, const void* v_seq,
              const void* k_depth, const void* v_depth,
