@@ -20,8 +20,11 @@
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (HIP device memory of the current
- *     device), owned by the caller.  The library allocates nothing and keeps
- *     no state between calls; calls on different streams may run concurrently.
+ *     device), owned by the caller.  The library allocates nothing.  Its only
+ *     state between calls is in its own static device memory: the launch
+ *     counters of long grids (see moda_fwd; each launch takes its own and
+ *     returns it to zero) and moda_bwd_noalloc's work array.  Calls on
+ *     different streams may run concurrently (moda_bwd_noalloc aside).
  *   - Tensors are dense, row-major, in the layouts stated per argument
  *     (no strides).  Element type is `dtype` (MODA_F32 or MODA_BF16) except
  *     lse, which is always float32.
