@@ -238,3 +238,48 @@ def test_bwd_counter_order_repeatable_and_concurrent():
     for i, g in enumerate(runs):
         for name, a, b in zip(NAMES, ref, g):
             assert torch.equal(a, b), f"call {i + 1}: {name} differs from the first call"
+
+
+def test_bwd_counter_nine_pairs():
+    """Nine (b, kv head) pairs (B = 3, Hkv = 3): the dQ and dK/dV grids
+    (1152 and 576 workgroups) take their tiles from nine per-pair queues,
+    workgroups moving on to the following pairs' queues once their own is
+    empty.  Sampled query groups, the last keys of every pair and the exact
+    gradient sums against the oracle; a second call bit-equal to the first."""
+    B, T, Hq, Hkv, d, L_d = 3, 8192, 6, 3, 128, 3
+    _say(f"bwd nine pairs: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L_d}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype="bf16", seed=6161)
+    dout = make_dout(B, T, Hq, d, dtype="bf16", seed=6162)
+    dev = torch.device("cuda:0")
+    qd, ksd, vsd, dd = q.to(dev), ks.to(dev), vs.to(dev), dout.to(dev)
+    kp, vp = moda.moda_pack_depth(kd.to(dev), vd.to(dev))
+    out, lse = moda.moda_fwd(qd, ksd, vsd, kp, vp, L_d)
+    g1 = moda.moda_bwd(qd, ksd, vsd, kp, vp, L_d, out, lse, dd)
+    g2 = moda.moda_bwd(qd, ksd, vsd, kp, vp, L_d, out, lse, dd)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, g1, g2):
+        assert torch.equal(a, b), f"second call: {name} differs"
+    dq, dks, dvs, dkd, dvd = [g.double().cpu().numpy() for g in g1]
+    G = Hq // Hkv
+    rng = np.random.default_rng(6163)
+    ts = sorted(set(rng.integers(0, T, 12).tolist()) | {0, T - 1})
+    groups = [(b, t, kvh) for b in range(B) for t in ts for kvh in range(Hkv)]
+    rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), groups=groups)
+    errs = {"dq": _rel_err(np.stack([dq[b, t, kvh * G:(kvh + 1) * G] for (b, t, kvh) in groups]), rq),
+            "dk_depth": _rel_err(np.stack([dkd[b, t, :, kvh] for (b, t, kvh) in groups]), rkd),
+            "dv_depth": _rel_err(np.stack([dvd[b, t, :, kvh] for (b, t, kvh) in groups]), rvd)}
+    errs.update(key_errors("tail", np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), dks, dvs, B, Hkv,
+                           tail_keys(T)))
+    do = np32(dout).astype(np.float64)
+    for b in range(B):
+        for kvh in range(Hkv):
+            sv = dvs[b, :, kvh].sum(0) + dvd[b, :, :, kvh].sum((0, 1))
+            l1v = np.abs(dvs[b, :, kvh]).sum(0) + np.abs(dvd[b, :, :, kvh]).sum((0, 1))
+            sk = dks[b, :, kvh].sum(0) + dkd[b, :, :, kvh].sum((0, 1))
+            l1k = np.abs(dks[b, :, kvh]).sum(0) + np.abs(dkd[b, :, :, kvh]).sum((0, 1))
+            errs[f"sum_dv[{b},{kvh}]"] = float((np.abs(sv - do[b, :, kvh * G:(kvh + 1) * G].sum((0, 1))) / l1v).max())
+            errs[f"sum_dk[{b},{kvh}]"] = float((np.abs(sk) / l1k).max())
+    tol = TOL_BWD[q.dtype]
+    _say("nine pairs: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{k} error {v} > {tol}"
