@@ -213,3 +213,46 @@ def test_counter_order_repeatable_and_concurrent():
         assert torch.equal(o, o0) and torch.equal(l, l0), f"call {i + 1} differs from the first"
     rows = sample_rows(B, T, Hq, n=512, seed=4243, tile_rows=(T - 1,))
     _check("counter order", inputs[0].dtype, *compare_rows(inputs, o0.cpu(), l0.cpu(), rows))
+
+
+def test_counter_order_under_graph_replay():
+    """A forward and an allocation-free backward on long grids (tiles from the
+    launch counters) recorded into a HIP graph: each replay, with eager work
+    and synchronisations between replays, equals the eager results bit for
+    bit (the recorded launches keep their counter slots, which each replay
+    returns to zero)."""
+    B, T, Hq, Hkv, d, L = 1, 16384, 16, 2, 128, 4
+    _say(f"graph replay: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L}")
+    from moda_inputs import make_dout
+    dev = torch.device("cuda:0")
+    q, ks, vs, kd, vd = [x.to(dev) for x in make_inputs(B, T, Hq, Hkv, d, L, dtype="bf16", seed=7171)]
+    dout = make_dout(B, T, Hq, d, dtype="bf16", seed=7172).to(dev)
+    kp, vp = moda.moda_pack_depth(kd, vd)
+    ref_o, ref_l = moda.moda_fwd(q, ks, vs, kp, vp, L)
+    ref_g = moda.moda_bwd(q, ks, vs, kp, vp, L, ref_o, ref_l, dout)
+    o = torch.empty_like(ref_o)
+    l = torch.empty_like(ref_l)
+    g = tuple(torch.empty_like(x) for x in ref_g)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        moda.moda_fwd(q, ks, vs, kp, vp, L, out=o, lse=l)
+        moda.moda_bwd_noalloc(q, ks, vs, kp, vp, L, o, l, dout, grads=g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moda.moda_fwd(q, ks, vs, kp, vp, L, out=o, lse=l)
+        moda.moda_bwd_noalloc(q, ks, vs, kp, vp, L, o, l, dout, grads=g)
+    for r in range(3):
+        o.zero_()
+        for x in g:
+            x.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), f"replay {r}: forward differs"
+        for name, a, b in zip(("dq", "dk_seq", "dv_seq", "dk_depth", "dv_depth"), ref_g, g):
+            assert torch.equal(a, b), f"replay {r}: {name} differs"
+        # eager work between replays, on the same counters' ring
+        moda.moda_fwd(q, ks, vs, kp, vp, L)
+        torch.cuda.synchronize()
