@@ -267,15 +267,16 @@ int moda_pack_depth(const void* k_depth, const void* v_depth, void* k_packed, vo
 // streams) use different slots as long as fewer than kTickSlots of them
 // overlap.  The per-device address comes from hipGetSymbolAddress, once per
 // device; without it a grid keeps the blockIdx order.
+constexpr int kMaxDevices = 64;   // GPUs per process the per-device state is kept for
 constexpr int kTickSlots = 1024;
 static __device__ __align__(256) uint32_t work_tick[moda::kTickWords * kTickSlots];
 static std::mutex g_tick_mu;
-static uint32_t* g_tick_ptr[64] = {};
+static uint32_t* g_tick_ptr[kMaxDevices] = {};
 static std::atomic<uint32_t> g_tick_next{0};
 
 static uint32_t* tick_slot() {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   uint32_t* base;
   {
     std::lock_guard<std::mutex> lock(g_tick_mu);
@@ -488,7 +489,6 @@ int moda_append_depth(const void* k_new, const void* v_new, void* k_packed, void
 // the first call there with that device current.
 constexpr long long kScratchFloats = 8LL << 20;                  // 32 MiB: B * Hq * T <= 4M rows
 static __device__ __align__(256) float scratch[kScratchFloats];
-constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static float* g_scratch_ptr[kMaxDevices] = {};
 
