@@ -29,7 +29,8 @@
  *     (no strides).  Element type is `dtype` (MODA_F32 or MODA_BF16) except
  *     lse, which is always float32.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default
- *     stream.  Every call only enqueues work and returns; results are ready
+ *     stream.  It must belong to the current device, which holds the
+ *     tensors (the library's per-device state is the current device's).  Every call only enqueues work and returns; results are ready
  *     after the stream is synchronised.
  *   - Arguments are validated before any HIP call is made.  A failed
  *     validation returns a nonzero moda_status and enqueues nothing.  A
