@@ -283,3 +283,36 @@ def test_bwd_counter_nine_pairs():
     _say("nine pairs: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
     for k, v in errs.items():
         assert v <= tol, f"{k} error {v} > {tol}"
+
+
+def test_bwd_ragged_long_grid():
+    """The backward on a long grid (dQ and dK/dV tiles from the launch
+    counters) with T = 20001, G = 8, L_d = 5: sampled query groups and the
+    last keys (partial last key tile) against the oracle, exact sums."""
+    B, T, Hq, Hkv, d, L_d = 1, 20001, 16, 2, 128, 5
+    _say(f"bwd ragged long grid: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L_d}")
+    q, ks, vs, kd, vd = make_inputs(B, T, Hq, Hkv, d, L_d, dtype="bf16", seed=8191)
+    dout = make_dout(B, T, Hq, d, dtype="bf16", seed=8192)
+    dq, dks, dvs, dkd, dvd = run_fwd_bwd(q, ks, vs, kd, vd, dout)
+    G = Hq // Hkv
+    rng = np.random.default_rng(8193)
+    ts = sorted(set(rng.integers(0, T, 16).tolist()) | {0, T - 33, T - 2, T - 1})
+    groups = [(0, t, kvh) for t in ts for kvh in range(Hkv)]
+    rq, rkd, rvd = moda_backward(np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), groups=groups)
+    errs = {"dq": _rel_err(np.stack([dq[b, t, kvh * G:(kvh + 1) * G] for (b, t, kvh) in groups]), rq),
+            "dk_depth": _rel_err(np.stack([dkd[b, t, :, kvh] for (b, t, kvh) in groups]), rkd),
+            "dv_depth": _rel_err(np.stack([dvd[b, t, :, kvh] for (b, t, kvh) in groups]), rvd)}
+    errs.update(key_errors("tail", np32(q), np32(ks), np32(vs), np32(kd), np32(vd), np32(dout), dks, dvs, B, Hkv,
+                           tail_keys(T)))
+    do = np32(dout).astype(np.float64)
+    for kvh in range(Hkv):
+        sv = dvs[0, :, kvh].sum(0) + dvd[0, :, :, kvh].sum((0, 1))
+        l1v = np.abs(dvs[0, :, kvh]).sum(0) + np.abs(dvd[0, :, :, kvh]).sum((0, 1))
+        sk = dks[0, :, kvh].sum(0) + dkd[0, :, :, kvh].sum((0, 1))
+        l1k = np.abs(dks[0, :, kvh]).sum(0) + np.abs(dkd[0, :, :, kvh]).sum((0, 1))
+        errs[f"sum_dv[{kvh}]"] = float((np.abs(sv - do[0, :, kvh * G:(kvh + 1) * G].sum((0, 1))) / l1v).max())
+        errs[f"sum_dk[{kvh}]"] = float((np.abs(sk) / l1k).max())
+    tol = TOL_BWD[q.dtype]
+    _say("bwd ragged: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"  (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{k} error {v} > {tol}"

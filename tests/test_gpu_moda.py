@@ -256,3 +256,16 @@ def test_counter_order_under_graph_replay():
         # eager work between replays, on the same counters' ring
         moda.moda_fwd(q, ks, vs, kp, vp, L)
         torch.cuda.synchronize()
+
+
+def test_ragged_long_grid_sampled_rows():
+    """A long grid (tiles from the launch counter) whose length is not a
+    multiple of the 64-key block or of the 32-key depth tile: T = 20001,
+    G = 8, L_d = 5.  Sampled rows (with the last positions, where the last
+    key block and the last depth tile are partial) against the oracle."""
+    B, T, Hq, Hkv, d, L = 1, 20001, 16, 2, 128, 5
+    _say(f"ragged long grid: B={B} T={T} Hq={Hq} Hkv={Hkv} d={d} L_d={L}")
+    inputs = make_inputs(B, T, Hq, Hkv, d, L, dtype="bf16", seed=8181)
+    rows = sample_rows(B, T, Hq, n=1024, seed=8182, tile_rows=(T - 1, T - 2, T - 33, 19968, 19967))
+    out, lse = run_gpu(*inputs)
+    _check("ragged long grid", inputs[0].dtype, *compare_rows(inputs, out, lse, rows))
