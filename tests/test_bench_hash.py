@@ -27,3 +27,14 @@ def test_code_only_keeps_strings_and_code_changes():
 def test_hash_is_stable():
     h = bench.kernel_source_hash()
     assert len(h) == 16 and h == bench.kernel_source_hash()
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so,
+    before touching a GPU."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
