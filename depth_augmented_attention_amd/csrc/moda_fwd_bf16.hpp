@@ -25,7 +25,9 @@
 //     wave: two waves per SIMD, and each K/V block staged in LDS serves 256
 //     rows (one workgroup per compute unit; +3% over four-wave workgroups
 //     with two per compute unit).  Grids too small to fill the GPU twice over
-//     with 256-row tiles use four-wave workgroups (128 rows) instead.
+//     with 256-row tiles use four-wave workgroups (128 rows) instead.  The
+//     eight-wave grids take their tiles from a per-launch counter in the
+//     order their workgroups start (see the work-item code below).
 //   * Probabilities are taken against the running max without forming the
 //     block's row max first; only when a lane's sum of them exceeds 2^8 (a
 //     score rose well above the max, or the first block) is the row max
